@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged-KV attention library on one MI355X.
+
+A step is one pass of the decode hot path over one batch: reshape_and_cache of
+the batch's new token (one row per sequence), the split-K partial pass, and the
+log-sum-exp merge. The workload is a Qwen3-0.6B-shaped single layer: 32
+sequences, 16 query / 8 KV heads, head_dim 128, bf16 q/K/V from N(0, 1),
+context lengths uniform in [128, 384], 16-token blocks drawn from a 4096-block
+pool. Inputs are resident in HBM before timing starts.
+
+The cache is far smaller than MI355X's 256 MB Infinity Cache would need to
+stay cold, so the timed loop rotates through R independent replicas (own
+pool, own block tables, own values); between two uses of one replica the other
+R - 1 replicas touch well over 256 MB, so every step reads its KV from HBM.
+Steps are launched from HIP graphs (each graph holds many steps) so that host
+launch cost does not pace the GPU.
+
+Output: one JSON line on stdout (everything else goes to stderr).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode KV GB/s (% HBM peak) + seq-steps/s; chunked-prefill MFMA util"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+KERNEL_FILES = ("paged_kv_attention_19_amd/csrc/decode.hip", "paged_kv_attention_19_amd/csrc/pkv_device.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_qwen3_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kv_bytes_per_token(num_kv_heads: int, head_dim: int, elem_bytes: int, scale_bytes: int = 0,
+                       layers: int = 1) -> int:
+    """Algorithmic KV bytes one token of one layer holds: K and V rows of every
+    KV head, plus their scales for int8."""
+    return layers * 2 * num_kv_heads * (head_dim * elem_bytes + scale_bytes)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_FILES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=8192)
+    ap.add_argument("--warmup", type=int, default=512)
+    ap.add_argument("--replicas", type=int, default=16)
+    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--max-tokens-per-split", type=int, default=128,
+                    help="num_splits[b] = ceil(n_b / this); 0 = one split per sequence")
+    ap.add_argument("--steps-per-graph", type=int, default=256)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=1902)
+    return ap.parse_args()
+
+
+class Replica:
+    """One independent copy of the workload, resident on the GPU."""
+
+    def __init__(self, step, dev, max_tokens_per_split):
+        import numpy as np
+        import torch
+
+        import paged_kv_attention_19_amd as pkv
+        self.step = step
+
+        def dt(a, kind):
+            if kind == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        self.cache = pkv.KVCache.allocate(step.num_blocks, step.num_kv_heads, step.head_dim, pkv.BF16, dev)
+        pkv.reshape_and_cache(dt(step.prefix_k, "bf16"), dt(step.prefix_v, "bf16"),
+                              dt(step.prefix_slots.astype(np.int64), "i64"), self.cache)
+        q, tables, ctx, ns = step.decode_batch()
+        self.q = dt(q, "bf16")
+        self.tables = dt(tables.astype(np.int32), "i32")
+        self.ctx = dt(ctx.astype(np.int32), "i32")
+        self.max_ns = int(ns.max())
+        self.ns = dt(ns.astype(np.int32), "i32")
+        self.new_k = dt(step.new_k, "bf16")
+        self.new_v = dt(step.new_v, "bf16")
+        self.new_slots = dt(step.new_slots.astype(np.int64), "i64")
+        B, Hq, D = q.shape
+        self.out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        wsb = pkv.decode_workspace_bytes(B, Hq, D, self.max_ns)
+        self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+        S = self.max_ns
+        flat = self.ws.view(torch.float32)
+        self.o_part = flat[: B * S * Hq * D].view(B, S, Hq, D)
+        self.lse_part = flat[B * S * Hq * D: B * S * Hq * (D + 1)].view(B, S, Hq)
+        self.tokens = int(ctx.sum())
+        self.kv_bytes = self.tokens * kv_bytes_per_token(step.num_kv_heads, step.head_dim, 2)
+        self.batch = B
+
+    def reshape(self):
+        import paged_kv_attention_19_amd as pkv
+        pkv.reshape_and_cache(self.new_k, self.new_v, self.new_slots, self.cache)
+
+    def decode(self):
+        import paged_kv_attention_19_amd as pkv
+        pkv.paged_attention_decode(self.q, self.cache, self.tables, self.ctx, self.ns, self.max_ns,
+                                   float(self.step.scale), out=self.out, out_lse=self.lse, workspace=self.ws)
+
+    def partials(self):
+        import paged_kv_attention_19_amd as pkv
+        if self.max_ns == 1:
+            self.decode()
+        else:
+            pkv.paged_attention_decode(self.q, self.cache, self.tables, self.ctx, self.ns, self.max_ns,
+                                       float(self.step.scale), workspace=self.ws, partials_only=True)
+
+    def combine(self):
+        import paged_kv_attention_19_amd as pkv
+        if self.max_ns == 1:
+            return
+        pkv.lse_combine(self.o_part, self.lse_part, self.ns, out=self.out, out_lse=self.lse)
+
+    def step_once(self):
+        self.reshape()
+        self.decode()
+
+
+def time_graphs(fn_per_step, reps, steps, steps_per_graph, warmup):
+    """Capture graphs of ``steps_per_graph`` consecutive steps (rotating over the
+    replicas) and replay them until exactly ``steps`` steps ran; returns seconds."""
+    import torch
+    R = len(reps)
+
+    def capture(n, start):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn_per_step(reps[(start + i) % R])
+        return g
+
+    per = max(1, min(steps_per_graph, steps))
+    per = max(R, (per // R) * R)          # whole rotations inside a graph
+    g_full = capture(per, 0)
+    rem = steps % per
+    g_rem = capture(rem, 0) if rem else None
+    torch.cuda.synchronize()
+    for _ in range(max(1, warmup // per)):
+        g_full.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps // per):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3
+
+
+def cpu_baseline(step, seconds):
+    """The oracle as it stands, on the host: one decode step (new-row write +
+    attention of every sequence and head) repeated for about ``seconds``."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    pool = oracle.OraclePool(step.num_blocks, step.num_kv_heads, step.block_size, step.head_dim, step.kv_dtype)
+    oracle.reshape_and_cache(pool, step.prefix_k, step.prefix_v, step.src_dtype, step.prefix_slots)
+    q, tables, ctx, _ = step.decode_batch()
+    q64 = oracle.decode_rows(q, step.q_dtype)
+    reps = 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while True:
+            oracle.reshape_and_cache(pool, step.new_k, step.new_v, step.src_dtype, step.new_slots)
+            oracle.paged_decode(q64, pool, tables, ctx, step.scale)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    per_step = el / reps
+    kvb = int(ctx.sum()) * kv_bytes_per_token(step.num_kv_heads, step.head_dim, 2)
+    return {"value": round(kvb / per_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full decode steps of one replica ({len(ctx)} sequences x {step.num_q_heads} heads, "
+                      f"{int(ctx.sum())} tokens), float64 NumPy, BLAS limited to 1 thread; "
+                      f"{per_step * 1e3:.1f} ms per step"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py measures one GPU: this build has no multi-GPU path (the decode shards by "
+            "sequence or KV head with no exchange; see the design notes). Run with --gpus 1.")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_attention_19_amd as pkv
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    pkv.lib()
+    mts = args.max_tokens_per_split or None
+
+    t0 = time.time()
+    reps = []
+    for r in range(args.replicas):
+        step = W.qwen3_decode(batch=args.batch, seed=args.seed + 1000 * r, max_tokens_per_split=mts)
+        reps.append(Replica(step, dev, mts))
+    torch.cuda.synchronize()
+    log(f"built {len(reps)} replicas in {time.time() - t0:.1f}s; max_ns={[r.max_ns for r in reps][:4]}...")
+
+    # eager reference of one step per replica, then check graph replays against it
+    eager = []
+    for r in reps:
+        r.step_once()
+    torch.cuda.synchronize()
+    for r in reps:
+        eager.append((r.out.clone(), r.lse.clone()))
+        r.out.fill_(float("nan"))
+        r.lse.fill_(float("nan"))
+
+    steps = args.steps
+    sec = time_graphs(lambda r: r.step_once(), reps, steps, args.steps_per_graph, args.warmup)
+    for r, (eo, el) in zip(reps, eager):
+        if not (torch.equal(r.out, eo) and torch.equal(r.lse, el)):
+            log("graph replay output differs from the eager step")
+            sys.exit(1)
+    R = len(reps)
+    kv_total = sum(reps[i % R].kv_bytes for i in range(steps))
+    seqs_total = sum(reps[i % R].batch for i in range(steps))
+    value = kv_total / sec / 1e9
+
+    # per-kernel launch durations: graphs holding one kind of launch
+    per_kernel = {}
+    n_k = min(steps, 4096)
+    sec_p = time_graphs(lambda r: r.partials(), reps, n_k, args.steps_per_graph, 64)
+    per_kernel["decode_partial"] = sec_p / n_k
+    if reps[0].max_ns > 1:
+        sec_c = time_graphs(lambda r: r.combine(), reps, n_k, args.steps_per_graph, 64)
+        per_kernel["lse_combine"] = sec_c / n_k
+    sec_r = time_graphs(lambda r: r.reshape(), reps, n_k, args.steps_per_graph, 64)
+    per_kernel["reshape_and_cache"] = sec_r / n_k
+    partial_bytes = sum(reps[i % R].kv_bytes for i in range(n_k)) / n_k
+    achieved = partial_bytes / per_kernel["decode_partial"] / 1e9
+
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("max_tokens_per_split") == args.max_tokens_per_split:
+            traffic = tr.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec / steps * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "qwen3_0.6b_layer_decode_step",
+            "batch": args.batch,
+            "num_q_heads": 16, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
+            "context_lens": "uniform[128,384]", "pool_blocks": 4096,
+            "max_tokens_per_split": args.max_tokens_per_split,
+            "replicas": R, "kv_bytes_per_step": int(kv_total / steps),
+            "parallelism": "none",
+        },
+        "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "seq_steps_per_s": round(seqs_total / sec, 1),
+        "kernel_us": {k: round(v * 1e6, 3) for k, v in per_kernel.items()},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_partial_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        line["cpu_baseline"] = cpu_baseline(reps[0].step, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,280 @@
+// C-ABI entry points of the paged-KV attention library (declared in pkv.h):
+// host-side argument checks, then kernel launches on the caller's stream.
+// Nothing here allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "pkv.h"
+#include "pkv_launch.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+pkv_status ok() {
+  g_error.clear();
+  return PKV_OK;
+}
+
+pkv_status hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+const char* dtype_name(int d) {
+  switch (d) {
+    case PKV_F32: return "F32";
+    case PKV_BF16: return "BF16";
+    case PKV_I8: return "I8";
+    default: return "?";
+  }
+}
+
+// Checks shared by every call that reads or writes the pool.
+pkv_status check_cache(const pkv_cache* c, const char* fn) {
+  if (c == nullptr) return fail(PKV_ERR_INVALID_ARG, "%s: cache descriptor is NULL", fn);
+  if (c->k == nullptr || c->v == nullptr) return fail(PKV_ERR_INVALID_ARG, "%s: cache k/v is NULL", fn);
+  if (c->num_blocks < 1 || c->num_kv_heads < 1)
+    return fail(PKV_ERR_INVALID_ARG, "%s: num_blocks=%d num_kv_heads=%d must be >= 1", fn, c->num_blocks,
+                c->num_kv_heads);
+  if (c->block_size != 16) return fail(PKV_ERR_UNSUPPORTED, "%s: block_size=%d (built: 16)", fn, c->block_size);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim=%d (built: 64, 128)", fn, c->head_dim);
+  if (c->kv_dtype != PKV_F32 && c->kv_dtype != PKV_BF16 && c->kv_dtype != PKV_I8)
+    return fail(PKV_ERR_INVALID_ARG, "%s: kv_dtype=%d is not F32/BF16/I8", fn, c->kv_dtype);
+  if (c->kv_dtype == PKV_I8 && (c->k_scale == nullptr || c->v_scale == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "%s: I8 cache needs k_scale and v_scale", fn);
+  if (!aligned16(c->k) || !aligned16(c->v)) return fail(PKV_ERR_INVALID_ARG, "%s: cache k/v not 16-byte aligned", fn);
+  if (c->kv_dtype == PKV_I8 && ((reinterpret_cast<uintptr_t>(c->k_scale) | reinterpret_cast<uintptr_t>(c->v_scale)) & 3u))
+    return fail(PKV_ERR_INVALID_ARG, "%s: scales not 4-byte aligned", fn);
+  const int64_t tile_elems = static_cast<int64_t>(c->num_kv_heads) * c->block_size * c->head_dim;
+  if (tile_elems * c->num_blocks > (int64_t(1) << 46))
+    return fail(PKV_ERR_INVALID_ARG, "%s: pool of %d blocks is implausibly large", fn, c->num_blocks);
+  return PKV_OK;
+}
+
+pkv_status check_group(int num_q_heads, int num_kv_heads, const char* fn) {
+  if (num_q_heads < 1) return fail(PKV_ERR_INVALID_ARG, "%s: num_q_heads=%d", fn, num_q_heads);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: num_q_heads=%d not a multiple of num_kv_heads=%d", fn, num_q_heads,
+                num_kv_heads);
+  const int g = num_q_heads / num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: GQA group size %d (built: 1, 2, 4, 8)", fn, g);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_error.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
+
+pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, int32_t src_dtype,
+                                 const int64_t* slot_mapping, int32_t num_tokens, const pkv_cache* cache,
+                                 void* stream) {
+  const char* fn = "pkv_reshape_and_cache";
+  if (pkv_status st = check_cache(cache, fn); st != PKV_OK) return st;
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "%s: num_tokens=%d", fn, num_tokens);
+  if (num_tokens == 0) return ok();
+  if (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "%s: k_new/v_new/slot_mapping is NULL", fn);
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(PKV_ERR_INVALID_ARG, "%s: k_new/v_new not 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: slot_mapping not 8-byte aligned", fn);
+  const int kv = cache->kv_dtype;
+  if (kv == PKV_I8) {
+    if (src_dtype != PKV_F32 && src_dtype != PKV_BF16)
+      return fail(PKV_ERR_INVALID_ARG, "%s: I8 cache takes F32 or BF16 rows, got %s", fn, dtype_name(src_dtype));
+  } else if (src_dtype != kv) {
+    return fail(PKV_ERR_INVALID_ARG, "%s: %s cache needs %s rows, got %s", fn, dtype_name(kv), dtype_name(kv),
+                dtype_name(src_dtype));
+  }
+  pkv::ReshapeParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.slots = slot_mapping;
+  p.k = cache->k;
+  p.v = cache->v;
+  p.k_scale = cache->k_scale;
+  p.v_scale = cache->v_scale;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.num_slots = static_cast<int64_t>(cache->num_blocks) * cache->block_size;
+  const hipError_t e = pkv::launch_reshape(p, src_dtype, kv, cache->head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t max_num_splits) {
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_num_splits <= 0) return 0;
+  if (max_num_splits == 1) return 0;
+  const size_t rows = static_cast<size_t>(batch) * max_num_splits * num_q_heads;
+  const size_t bytes = rows * (static_cast<size_t>(head_dim) + 1) * sizeof(float);
+  return (bytes + 255) & ~static_cast<size_t>(255);
+}
+
+pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                      const pkv_cache* cache, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                      const int32_t* num_splits, int32_t max_num_splits, float scale, float* out,
+                                      float* out_lse, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "pkv_paged_attention_decode";
+  if (pkv_status st = check_cache(cache, fn); st != PKV_OK) return st;
+  if (batch < 0) return fail(PKV_ERR_INVALID_ARG, "%s: batch=%d", fn, batch);
+  if (pkv_status st = check_group(num_q_heads, cache->num_kv_heads, fn); st != PKV_OK) return st;
+  if (batch == 0) return ok();
+  if (batch > 65535) return fail(PKV_ERR_UNSUPPORTED, "%s: batch=%d (built: <= 65535)", fn, batch);
+  if (q_dtype != PKV_F32 && q_dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID_ARG, "%s: q_dtype=%s (F32 or BF16)", fn, dtype_name(q_dtype));
+  if (q == nullptr || block_tables == nullptr || context_lens == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "%s: q/block_tables/context_lens is NULL", fn);
+  if (out == nullptr && max_num_splits == 1)
+    return fail(PKV_ERR_INVALID_ARG, "%s: out is NULL (partials-only mode needs max_num_splits > 1)", fn);
+  if (!aligned16(q) || !aligned16(out)) return fail(PKV_ERR_INVALID_ARG, "%s: q/out not 16-byte aligned", fn);
+  if (max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "%s: max_blocks_per_seq=%d", fn, max_blocks_per_seq);
+  if (max_num_splits < 1 || max_num_splits > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "%s: max_num_splits=%d (1..65535)", fn, max_num_splits);
+  if (max_num_splits > 1 && num_splits == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "%s: num_splits is NULL with max_num_splits=%d", fn, max_num_splits);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  const int D = cache->head_dim;
+  const size_t need = pkv_decode_workspace_bytes(batch, num_q_heads, D, max_num_splits);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace == nullptr ? size_t(0) : workspace_bytes);
+  if (need > 0 && !aligned16(workspace)) return fail(PKV_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
+
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool direct = max_num_splits == 1;
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = direct ? nullptr : o_part + static_cast<size_t>(batch) * max_num_splits * num_q_heads * D;
+
+  pkv::DecodeParams p{};
+  p.q = q;
+  p.k = cache->k;
+  p.v = cache->v;
+  p.k_scale = cache->k_scale;
+  p.v_scale = cache->v_scale;
+  p.tables = block_tables;
+  p.ctx = context_lens;
+  p.nsplits = num_splits;
+  p.o = direct ? out : o_part;
+  p.lse = direct ? out_lse : lse_part;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_blocks = cache->num_blocks;
+  p.max_ns = max_num_splits;
+  p.direct = direct ? 1 : 0;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const int group = num_q_heads / cache->num_kv_heads;
+  hipError_t e = pkv::launch_decode_partial(p, cache->kv_dtype, q_dtype, D, group, batch, st);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (!direct && out != nullptr) {
+    pkv::CombineParams cp{};
+    cp.o_part = o_part;
+    cp.lse_part = lse_part;
+    cp.nsplits = num_splits;
+    cp.out = out;
+    cp.out_lse = out_lse;
+    cp.batch = batch;
+    cp.num_q_heads = num_q_heads;
+    cp.max_ns = max_num_splits;
+    e = pkv::launch_combine(cp, D, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+  }
+  return ok();
+}
+
+pkv_status pkv_lse_combine(const float* o_part, const float* lse_part, int32_t batch, int32_t num_q_heads,
+                           int32_t head_dim, int32_t max_num_splits, const int32_t* num_splits, float* out,
+                           float* out_lse, void* stream) {
+  const char* fn = "pkv_lse_combine";
+  if (batch < 0 || num_q_heads < 1 || max_num_splits < 1)
+    return fail(PKV_ERR_INVALID_ARG, "%s: batch=%d num_q_heads=%d max_num_splits=%d", fn, batch, num_q_heads,
+                max_num_splits);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim=%d (built: 64, 128)", fn, head_dim);
+  if (batch == 0) return ok();
+  if (static_cast<int64_t>(batch) * num_q_heads > (int64_t(1) << 30))
+    return fail(PKV_ERR_INVALID_ARG, "%s: batch * num_q_heads too large", fn);
+  if (o_part == nullptr || lse_part == nullptr || num_splits == nullptr || out == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "%s: o_part/lse_part/num_splits/out is NULL", fn);
+  pkv::CombineParams cp{};
+  cp.o_part = o_part;
+  cp.lse_part = lse_part;
+  cp.nsplits = num_splits;
+  cp.out = out;
+  cp.out_lse = out_lse;
+  cp.batch = batch;
+  cp.num_q_heads = num_q_heads;
+  cp.max_ns = max_num_splits;
+  const hipError_t e = pkv::launch_combine(cp, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                                       const int32_t* cu_q_lens, int32_t max_q_len, const pkv_cache* cache,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, float scale, float* out, float* out_lse,
+                                       void* stream) {
+  const char* fn = "pkv_paged_attention_chunked";
+  if (pkv_status st = check_cache(cache, fn); st != PKV_OK) return st;
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "%s: num_seqs=%d", fn, num_seqs);
+  if (pkv_status st = check_group(num_q_heads, cache->num_kv_heads, fn); st != PKV_OK) return st;
+  if (num_seqs == 0) return ok();
+  if (q_dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "%s: q_dtype=%s (built: BF16)", fn, dtype_name(q_dtype));
+  if (cache->kv_dtype == PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: F32 cache (built: BF16, I8)", fn);
+  if (cache->head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim=%d (built: 128)", fn, cache->head_dim);
+  if (q == nullptr || cu_q_lens == nullptr || block_tables == nullptr || context_lens == nullptr || out == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "%s: q/cu_q_lens/block_tables/context_lens/out is NULL", fn);
+  if (!aligned16(q) || !aligned16(out)) return fail(PKV_ERR_INVALID_ARG, "%s: q/out not 16-byte aligned", fn);
+  if (max_q_len < 1) return fail(PKV_ERR_INVALID_ARG, "%s: max_q_len=%d", fn, max_q_len);
+  if (max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "%s: max_blocks_per_seq=%d", fn, max_blocks_per_seq);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  pkv::ChunkedParams p{};
+  p.q = q;
+  p.k = cache->k;
+  p.v = cache->v;
+  p.k_scale = cache->k_scale;
+  p.v_scale = cache->v_scale;
+  p.tables = block_tables;
+  p.ctx = context_lens;
+  p.cu_q = cu_q_lens;
+  p.out = out;
+  p.lse = out_lse;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_blocks = cache->num_blocks;
+  p.max_q_len = max_q_len;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t e = pkv::launch_chunked(p, cache->kv_dtype, cache->head_dim, num_q_heads / cache->num_kv_heads,
+                                           static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(PKV_ERR_UNSUPPORTED, "%s: this configuration is not built", fn);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+}  // extern "C"

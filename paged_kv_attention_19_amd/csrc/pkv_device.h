@@ -1,0 +1,104 @@
+// Device-side helpers shared by the gfx950 kernels of the paged-KV attention
+// library: element decoding, wavefront reductions and small vector types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv.h"
+
+namespace pkv {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 16;                 // tokens per KV block (the only size built)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// ---- element decoding ------------------------------------------------------
+
+// bfloat16 pair packed in one dword -> two floats (low half first). A bf16 is
+// the upper 16 bits of the binary32 with the same value.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float i8_at(uint32_t w, int byte) {
+  return static_cast<float>(static_cast<int8_t>((w >> (8 * byte)) & 0xffu));
+}
+
+// 16 bytes of a row -> EPL floats.
+template <int KV>
+__device__ __forceinline__ void unpack16(const uint4& x, float* f) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  if constexpr (KV == PKV_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+  } else if constexpr (KV == PKV_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(w[i]);
+      f[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) f[4 * i + b] = i8_at(w[i], b);
+    }
+  }
+}
+
+template <int KV>
+struct KvGeom {
+  static constexpr int kEsize = KV == PKV_F32 ? 4 : (KV == PKV_BF16 ? 2 : 1);
+  static constexpr int kEpl = 16 / kEsize;   // elements a lane holds per 16-byte load
+};
+
+// ---- cross-lane reductions -------------------------------------------------
+// DPP controls (GCN/CDNA encoding): quad permutes and in-row mirrors.
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W lanes (W in 1,2,4,8,16,32,64); every lane of
+// the group receives the total. Within a 16-lane row the steps are DPP moves;
+// across rows they are LDS-crossbar shuffles.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (W >= 2) x += dpp<kDppQuadXor1>(x);
+  if constexpr (W >= 4) x += dpp<kDppQuadXor2>(x);
+  if constexpr (W >= 8) x += dpp<kDppRowHalfMirror>(x);
+  if constexpr (W >= 16) x += dpp<kDppRowMirror>(x);
+  if constexpr (W >= 32) x += __shfl_xor(x, 16);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float x) {
+#pragma unroll
+  for (int m = 1; m < W; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_read_exec() & __ballot(p); }
+
+__device__ __forceinline__ int readlane(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+__device__ __forceinline__ float qnan() { return __builtin_nanf(""); }
+
+}  // namespace pkv

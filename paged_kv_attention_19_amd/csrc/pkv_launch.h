@@ -1,0 +1,86 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel files.
+// Kernel parameter blocks are plain structs passed by value to the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv.h"
+
+namespace pkv {
+
+struct ReshapeParams {
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slots;
+  void* k;
+  void* v;
+  float* k_scale;
+  float* v_scale;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int64_t num_slots;
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* tables;
+  const int32_t* ctx;
+  const int32_t* nsplits;  // unused when direct
+  float* o;                // out (direct) or o_part
+  float* lse;              // out_lse (direct, may be null) or lse_part
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t max_ns;
+  int32_t direct;          // 1: one split per sequence, normalised output to o/lse
+  float scale_log2;        // softmax scale * log2(e)
+};
+
+struct CombineParams {
+  const float* o_part;
+  const float* lse_part;
+  const int32_t* nsplits;
+  float* out;
+  float* out_lse;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t max_ns;
+};
+
+struct ChunkedParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* tables;
+  const int32_t* ctx;
+  const int32_t* cu_q;
+  float* out;
+  float* lse;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t max_q_len;
+  float scale_log2;
+};
+
+// Each launcher returns hipSuccess or the launch error; it assumes the host
+// checks of api.hip have passed (supported dtypes, sizes, group size).
+hipError_t launch_reshape(const ReshapeParams& p, int src_dtype, int kv_dtype, int head_dim,
+                          hipStream_t stream);
+hipError_t launch_decode_partial(const DecodeParams& p, int kv_dtype, int q_dtype, int head_dim,
+                                 int group, int batch, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_chunked(const ChunkedParams& p, int kv_dtype, int head_dim, int group,
+                          hipStream_t stream);
+
+}  // namespace pkv

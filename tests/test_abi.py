@@ -1,0 +1,111 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad host-side arguments before launching anything.
+Every call here fails a host check, so no kernel is ever launched."""
+
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+
+import paged_kv_attention_19_amd as pkv
+from paged_kv_attention_19_amd import _Cache
+
+FAKE = 0x10000  # never dereferenced: every call below fails a host check first
+
+
+def cache(**kw):
+    d = dict(num_blocks=8, block_size=16, num_kv_heads=2, head_dim=64, kv_dtype=pkv.BF16, k=FAKE, v=FAKE,
+             k_scale=None, v_scale=None)
+    d.update(kw)
+    return _Cache(d["num_blocks"], d["block_size"], d["num_kv_heads"], d["head_dim"], d["kv_dtype"], d["k"], d["v"],
+                  d["k_scale"], d["v_scale"])
+
+
+def test_library_exports_every_header_function():
+    L = pkv.lib()
+    names = pkv.exported_symbols()
+    assert {"pkv_reshape_and_cache", "pkv_paged_attention_decode", "pkv_paged_attention_chunked",
+            "pkv_lse_combine", "pkv_decode_workspace_bytes", "pkv_last_error", "pkv_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert "gfx950" in pkv.version()
+
+
+def test_workspace_bytes():
+    assert pkv.decode_workspace_bytes(32, 16, 128, 1) == 0
+    assert pkv.decode_workspace_bytes(0, 16, 128, 4) == 0
+    b = pkv.decode_workspace_bytes(32, 16, 128, 4)
+    assert b >= 32 * 4 * 16 * 129 * 4 and b % 256 == 0
+
+
+def dec(c, **kw):
+    a = dict(q=FAKE, q_dtype=pkv.BF16, batch=3, hq=4, tables=FAKE, maxb=4, ctx=FAKE, ns=FAKE, max_ns=2, scale=0.125,
+             out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    return pkv.lib().pkv_paged_attention_decode(a["q"], a["q_dtype"], a["batch"], a["hq"], ctypes.byref(c), a["tables"],
+                                                a["maxb"], a["ctx"], a["ns"], a["max_ns"], a["scale"], a["out"],
+                                                a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("ckw,kw,status", [
+    (dict(block_size=32), {}, -2),
+    (dict(head_dim=96), {}, -2),
+    (dict(num_kv_heads=3), {}, -1),            # 4 q heads not a multiple of 3
+    (dict(num_kv_heads=2), dict(hq=6), -2),    # group of 3 not built
+    (dict(kv_dtype=7), {}, -1),
+    (dict(kv_dtype=pkv.I8), {}, -1),           # int8 without scales
+    (dict(k=None), {}, -1),
+    (dict(k=FAKE + 4), {}, -1),                # misaligned pool
+    (dict(num_blocks=0), {}, -1),
+    ({}, dict(q=None), -1),
+    ({}, dict(q_dtype=pkv.I8), -1),
+    ({}, dict(out=FAKE + 8), -1),
+    ({}, dict(maxb=0), -1),
+    ({}, dict(max_ns=0), -1),
+    ({}, dict(ns=None), -1),
+    ({}, dict(ws=None), -3),
+    ({}, dict(ws_bytes=100), -3),
+    ({}, dict(scale=float("inf")), -1),
+    ({}, dict(batch=-1), -1),
+])
+def test_decode_rejects_bad_arguments(ckw, kw, status):
+    assert dec(cache(**ckw), **kw) == status
+    assert pkv.lib().pkv_last_error().decode().startswith("pkv_paged_attention_decode")
+
+
+def test_reshape_rejects_bad_arguments():
+    L = pkv.lib()
+    c = cache()
+    assert L.pkv_reshape_and_cache(FAKE, FAKE, pkv.F32, FAKE, 4, ctypes.byref(c), None) == -1   # bf16 cache, f32 rows
+    assert L.pkv_reshape_and_cache(None, FAKE, pkv.BF16, FAKE, 4, ctypes.byref(c), None) == -1
+    assert L.pkv_reshape_and_cache(FAKE, FAKE, pkv.BF16, FAKE + 4, 4, ctypes.byref(c), None) == -1
+    assert L.pkv_reshape_and_cache(FAKE, FAKE, pkv.BF16, FAKE, -1, ctypes.byref(c), None) == -1
+    ci8 = cache(kv_dtype=pkv.I8, k_scale=FAKE, v_scale=FAKE)
+    assert L.pkv_reshape_and_cache(FAKE, FAKE, pkv.I8, FAKE, 4, ctypes.byref(ci8), None) == -1
+    assert L.pkv_reshape_and_cache(FAKE, FAKE, pkv.BF16, FAKE, 0, ctypes.byref(c), None) == 0  # nothing to do
+    assert L.pkv_reshape_and_cache(FAKE, FAKE, pkv.BF16, FAKE, 4, None, None) == -1
+
+
+def test_chunked_and_combine_reject_bad_arguments():
+    L = pkv.lib()
+    c = cache(head_dim=128)
+    args = [FAKE, pkv.BF16, 2, 4, FAKE, 64, ctypes.byref(c), FAKE, 8, FAKE, 0.1, FAKE, None, None]
+    bad = list(args); bad[1] = pkv.F32
+    assert L.pkv_paged_attention_chunked(*bad) == -2
+    bad = list(args); bad[6] = ctypes.byref(cache(head_dim=128, kv_dtype=pkv.F32))
+    assert L.pkv_paged_attention_chunked(*bad) == -2
+    bad = list(args); bad[5] = 0
+    assert L.pkv_paged_attention_chunked(*bad) == -1
+    bad = list(args); bad[4] = None
+    assert L.pkv_paged_attention_chunked(*bad) == -1
+    assert L.pkv_lse_combine(FAKE, FAKE, 2, 4, 96, 2, FAKE, FAKE, None, None) == -2
+    assert L.pkv_lse_combine(None, FAKE, 2, 4, 128, 2, FAKE, FAKE, None, None) == -1
+    assert L.pkv_lse_combine(FAKE, FAKE, 2, 4, 128, 0, FAKE, FAKE, None, None) == -1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(2, 4, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        pkv.paged_attention_decode(q, None, q, q, None, 1, 0.1)
