@@ -57,20 +57,54 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+# name -> (builder(seed, max_tokens_per_split), default replicas, default split size, config text)
+WORKLOADS = {
+    "qwen3_decode": (lambda W, seed, mts, batch: W.qwen3_decode(batch=batch, seed=seed, max_tokens_per_split=mts or None),
+                     16, 0, {"workload": "qwen3_0.6b_layer_decode_step", "context_lens": "uniform[128,384]",
+                             "pool_blocks": 4096}),
+    "ragged_decode": (lambda W, seed, mts, batch: W.ragged_decode(seed=seed, max_tokens_per_split=mts or 512),
+                      1, 512, {"workload": "ragged_decode_b256", "context_lens": "log-uniform[64,8192]"}),
+    "long_decode": (lambda W, seed, mts, batch: W.long_decode(seed=seed, num_splits=(32768 // mts) if mts else 64),
+                    1, 512, {"workload": "long_decode_b8_32k", "context_lens": "32768"}),
+    "mixed_int8_decode": (lambda W, seed, mts, batch: W.mixed_int8(seed=seed, max_tokens_per_split=mts or 512),
+                          1, 512, {"workload": "mixed_int8_step_decode_rows", "context_lens": "uniform[256,4096]"}),
+}
+DEFAULT_SEEDS = {"qwen3_decode": 1902, "ragged_decode": 1903, "long_decode": 1904, "mixed_int8_decode": 1905}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=8192)
     ap.add_argument("--warmup", type=int, default=512)
-    ap.add_argument("--replicas", type=int, default=16)
+    ap.add_argument("--replicas", type=int, default=None,
+                    help="independent copies rotated through (default: 16 for the Qwen3 step, else 1)")
     ap.add_argument("--batch", type=int, default=32)
-    ap.add_argument("--max-tokens-per-split", type=int, default=128,
-                    help="num_splits[b] = ceil(n_b / this); 0 = one split per sequence")
+    ap.add_argument("--max-tokens-per-split", type=int, default=None,
+                    help="num_splits[b] = ceil(n_b / this); 0 = one split per sequence "
+                         "(default: 0 for the Qwen3 step, 512 for the others)")
     ap.add_argument("--steps-per-graph", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--seed", type=int, default=1902)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--workload", default="qwen3_decode", choices=sorted(WORKLOADS),
+                    help="the step's shape (default: the Qwen3-0.6B decode step)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES, 8 times (to scale HBM counters)")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes: int) -> None:
+    """A plain copy kernel of known size: FETCH_SIZE / WRITE_SIZE of its dispatches
+    give the factor between the counters and bytes actually moved."""
+    import torch
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "copies": 8}), flush=True)
 
 
 class Replica:
@@ -88,29 +122,34 @@ class Replica:
                 return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-        self.cache = pkv.KVCache.allocate(step.num_blocks, step.num_kv_heads, step.head_dim, pkv.BF16, dev)
-        pkv.reshape_and_cache(dt(step.prefix_k, "bf16"), dt(step.prefix_v, "bf16"),
+        code = {"f32": pkv.F32, "bf16": pkv.BF16, "i8": pkv.I8}
+        self.cache = pkv.KVCache.allocate(step.num_blocks, step.num_kv_heads, step.head_dim, code[step.kv_dtype], dev)
+        pkv.reshape_and_cache(dt(step.prefix_k, step.src_dtype), dt(step.prefix_v, step.src_dtype),
                               dt(step.prefix_slots.astype(np.int64), "i64"), self.cache)
         q, tables, ctx, ns = step.decode_batch()
-        self.q = dt(q, "bf16")
+        self.q = dt(q, step.q_dtype)
         self.tables = dt(tables.astype(np.int32), "i32")
         self.ctx = dt(ctx.astype(np.int32), "i32")
         self.max_ns = int(ns.max())
         self.ns = dt(ns.astype(np.int32), "i32")
-        self.new_k = dt(step.new_k, "bf16")
-        self.new_v = dt(step.new_v, "bf16")
-        self.new_slots = dt(step.new_slots.astype(np.int64), "i64")
+        # the step's new rows: one per decode sequence (chunk rows belong to the chunked pass)
+        dec_rows = np.concatenate([np.arange(step.cu_q_lens[i], step.cu_q_lens[i + 1]) for i in step.decode_idx])
+        self.new_k = dt(step.new_k[dec_rows], step.src_dtype)
+        self.new_v = dt(step.new_v[dec_rows], step.src_dtype)
+        self.new_slots = dt(step.new_slots[dec_rows].astype(np.int64), "i64")
         B, Hq, D = q.shape
         self.out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
         self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
         wsb = pkv.decode_workspace_bytes(B, Hq, D, self.max_ns)
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
         S = self.max_ns
-        flat = self.ws.view(torch.float32)
-        self.o_part = flat[: B * S * Hq * D].view(B, S, Hq, D)
-        self.lse_part = flat[B * S * Hq * D: B * S * Hq * (D + 1)].view(B, S, Hq)
+        if S > 1:
+            flat = self.ws.view(torch.float32)
+            self.o_part = flat[: B * S * Hq * D].view(B, S, Hq, D)
+            self.lse_part = flat[B * S * Hq * D: B * S * Hq * (D + 1)].view(B, S, Hq)
         self.tokens = int(ctx.sum())
-        self.kv_bytes = self.tokens * kv_bytes_per_token(step.num_kv_heads, step.head_dim, 2)
+        eb, sb = {"f32": (4, 0), "bf16": (2, 0), "i8": (1, 4)}[step.kv_dtype]
+        self.kv_bytes = self.tokens * kv_bytes_per_token(step.num_kv_heads, step.head_dim, eb, sb)
         self.batch = B
 
     def reshape(self):
@@ -176,32 +215,34 @@ def time_graphs(fn_per_step, reps, steps, steps_per_graph, warmup):
 
 
 def cpu_baseline(step, seconds):
-    """The oracle as it stands, on the host: one decode step (new-row write +
-    attention of every sequence and head) repeated for about ``seconds``."""
-    import numpy as np
+    """The oracle as it stands, on the host: decode sequences of the step one at
+    a time (gather through the block table + float64 attention for every query
+    head), cycling through the batch for about ``seconds``."""
     from threadpoolctl import threadpool_limits
 
     import oracle
     pool = oracle.OraclePool(step.num_blocks, step.num_kv_heads, step.block_size, step.head_dim, step.kv_dtype)
     oracle.reshape_and_cache(pool, step.prefix_k, step.prefix_v, step.src_dtype, step.prefix_slots)
+    oracle.reshape_and_cache(pool, step.new_k, step.new_v, step.src_dtype, step.new_slots)
     q, tables, ctx, _ = step.decode_batch()
     q64 = oracle.decode_rows(q, step.q_dtype)
-    reps = 0
+    eb, sb = {"f32": (4, 0), "bf16": (2, 0), "i8": (1, 4)}[step.kv_dtype]
+    per_tok = kv_bytes_per_token(step.num_kv_heads, step.head_dim, eb, sb)
+    done_bytes = 0
+    seqs = 0
     with threadpool_limits(1):
         t0 = time.perf_counter()
         while True:
-            oracle.reshape_and_cache(pool, step.new_k, step.new_v, step.src_dtype, step.new_slots)
-            oracle.paged_decode(q64, pool, tables, ctx, step.scale)
-            reps += 1
+            b = seqs % len(ctx)
+            oracle.paged_decode(q64[b:b + 1], pool, tables[b:b + 1], ctx[b:b + 1], step.scale)
+            done_bytes += int(ctx[b]) * per_tok
+            seqs += 1
             el = time.perf_counter() - t0
             if el >= seconds:
                 break
-    per_step = el / reps
-    kvb = int(ctx.sum()) * kv_bytes_per_token(step.num_kv_heads, step.head_dim, 2)
-    return {"value": round(kvb / per_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full decode steps of one replica ({len(ctx)} sequences x {step.num_q_heads} heads, "
-                      f"{int(ctx.sum())} tokens), float64 NumPy, BLAS limited to 1 thread; "
-                      f"{per_step * 1e3:.1f} ms per step"}
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{seqs} sequence decodes ({min(seqs, len(ctx))} distinct of the step's {len(ctx)}; "
+                      f"{done_bytes / 1e6:.1f} MB of KV) in {el:.1f} s, float64 NumPy, BLAS limited to 1 thread"}
 
 
 def main():
@@ -212,7 +253,10 @@ def main():
             "sequence or KV head with no exchange; see the design notes). Run with --gpus 1.")
         sys.exit(2)
 
-    import numpy as np
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
     import torch
 
     import paged_kv_attention_19_amd as pkv
@@ -223,13 +267,17 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     pkv.lib()
-    mts = args.max_tokens_per_split or None
-
+    build, default_reps, default_mts, cfg_text = WORKLOADS[args.workload]
+    if args.max_tokens_per_split is None:
+        args.max_tokens_per_split = default_mts
+    if args.replicas is None:
+        args.replicas = default_reps
+    seed0 = DEFAULT_SEEDS[args.workload] if args.seed is None else args.seed
     t0 = time.time()
     reps = []
     for r in range(args.replicas):
-        step = W.qwen3_decode(batch=args.batch, seed=args.seed + 1000 * r, max_tokens_per_split=mts)
-        reps.append(Replica(step, dev, mts))
+        step = build(W, seed0 + 1000 * r, args.max_tokens_per_split, args.batch)
+        reps.append(Replica(step, dev, args.max_tokens_per_split))
     torch.cuda.synchronize()
     log(f"built {len(reps)} replicas in {time.time() - t0:.1f}s; max_ns={[r.max_ns for r in reps][:4]}...")
 
@@ -271,7 +319,8 @@ def main():
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("max_tokens_per_split") == args.max_tokens_per_split:
+        if (tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == args.workload
+                and tr.get("max_tokens_per_split") == args.max_tokens_per_split):
             traffic = tr.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         pass
@@ -287,17 +336,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": {"bf16": "bf16", "f32": "f32", "i8": "i8 kv / bf16 q"}[reps[0].step.kv_dtype],
         "data": "synthetic",
-        "config": {
-            "workload": "qwen3_0.6b_layer_decode_step",
-            "batch": args.batch,
+        "config": dict(cfg_text, **{
+            "batch": reps[0].batch,
             "num_q_heads": 16, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
-            "context_lens": "uniform[128,384]", "pool_blocks": 4096,
             "max_tokens_per_split": args.max_tokens_per_split,
             "replicas": R, "kv_bytes_per_step": int(kv_total / steps),
             "parallelism": "none",
-        },
+        }),
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(seqs_total / sec, 1),
         "kernel_us": {k: round(v * 1e6, 3) for k, v in per_kernel.items()},

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "pkv.h"
@@ -77,6 +78,20 @@ pkv_status check_group(int num_q_heads, int num_kv_heads, const char* fn) {
   if (g != 1 && g != 2 && g != 4 && g != 8)
     return fail(PKV_ERR_UNSUPPORTED, "%s: GQA group size %d (built: 1, 2, 4, 8)", fn, g);
   return PKV_OK;
+}
+
+// Wavefronts per decode workgroup. A workgroup reduces one split; its blocks
+// are dealt to the wavefronts round-robin. Four wavefronts (one per SIMD)
+// measured best on MI355X for every decode shape tried, from 8-block splits
+// to 32-block ones: more add per-wave setup and merge work, fewer leave
+// SIMDs idle. PKV_DECODE_WAVES (2, 4 or 8) overrides the choice, for tuning.
+int decode_waves(int /*max_blocks_per_seq*/, int /*max_num_splits*/) {
+  static const int forced = [] {
+    const char* e = std::getenv("PKV_DECODE_WAVES");
+    const int v = e ? std::atoi(e) : 0;
+    return (v == 2 || v == 4 || v == 8) ? v : 0;
+  }();
+  return forced ? forced : 4;
 }
 
 }  // namespace
@@ -185,8 +200,15 @@ pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t ba
   p.max_ns = max_num_splits;
   p.direct = direct ? 1 : 0;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.batch = batch;
   const int group = num_q_heads / cache->num_kv_heads;
-  hipError_t e = pkv::launch_decode_partial(p, cache->kv_dtype, q_dtype, D, group, batch, st);
+  const int waves = decode_waves(max_blocks_per_seq, max_num_splits);
+  hipError_t e;
+  switch (cache->kv_dtype) {
+    case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, waves, st); break;
+    case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, waves, st); break;
+    default: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, waves, st); break;
+  }
   if (e != hipSuccess) return hip_fail(e, fn);
   if (!direct && out != nullptr) {
     pkv::CombineParams cp{};

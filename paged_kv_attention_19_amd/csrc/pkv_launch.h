@@ -33,6 +33,7 @@ struct DecodeParams {
   const int32_t* nsplits;  // unused when direct
   float* o;                // out (direct) or o_part
   float* lse;              // out_lse (direct, may be null) or lse_part
+  int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t max_blocks;
@@ -77,8 +78,14 @@ struct ChunkedParams {
 // checks of api.hip have passed (supported dtypes, sizes, group size).
 hipError_t launch_reshape(const ReshapeParams& p, int src_dtype, int kv_dtype, int head_dim,
                           hipStream_t stream);
-hipError_t launch_decode_partial(const DecodeParams& p, int kv_dtype, int q_dtype, int head_dim,
-                                 int group, int batch, hipStream_t stream);
+// Decode partial pass, one entry per KV element type; `waves` (2, 4, 8)
+// is the number of wavefronts per workgroup.
+hipError_t launch_decode_partial_f32(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves,
+                                     hipStream_t stream);
+hipError_t launch_decode_partial_bf16(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves,
+                                      hipStream_t stream);
+hipError_t launch_decode_partial_i8(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves,
+                                    hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_chunked(const ChunkedParams& p, int kv_dtype, int head_dim, int group,
                           hipStream_t stream);
