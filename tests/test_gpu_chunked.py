@@ -1,0 +1,94 @@
+"""GPU parity: chunked prefill (causal query chunks over a paged prefix, MFMA
+kernel) against the oracle, at the tolerance of the decode tests."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads as W
+from tests import gpu_side as G
+from tests import oracle_side as O
+
+pytestmark = pytest.mark.gpu
+
+
+def check(got, ref, what):
+    st = O.compare(got, ref)
+    assert st["ok"], f"{what}: {st}"
+    return st
+
+
+def run_and_check(step, gpu):
+    cache = G.build_cache(step, gpu)
+    out, lse = G.run_chunked(step, cache, gpu)
+    ro, rl = O.chunked(step, O.pool(step))
+    check(out, ro, "out")
+    check(lse, rl, "lse")
+    return cache
+
+
+def test_mixed_int8_prefill_full_size(gpu):
+    """4 chunks of 512 rows over a 1536-token prefix, int8 KV: every output."""
+    step = W.mixed_int8(num_decode=4)
+    run_and_check(step, gpu)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("lens", [
+    ([64], [64]),                  # no prefix, one full tile
+    ([200, 77, 1, 130], [70, 77, 1, 65]),  # ragged chunks and prefixes
+    ([1000, 33], [300, 17]),
+])
+def test_chunked_shapes(gpu, kv, lens):
+    ctx, ql = lens
+    step = W.make_step(f"ch_{kv}", ctx, ql, num_q_heads=16, num_kv_heads=8, head_dim=128, kv_dtype=kv,
+                       src_dtype="bf16", seed=80 + len(ctx))
+    run_and_check(step, gpu)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2), (16, 4), (16, 2)])
+def test_chunked_group_sizes(gpu, Hq, Hkv):
+    step = W.make_step(f"grp{Hq}_{Hkv}", [150, 96], [100, 40], num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,
+                       kv_dtype="bf16", seed=90 + Hq)
+    run_and_check(step, gpu)
+
+
+def test_chunk_rows_match_decode_at_their_positions(gpu):
+    """Cross-path: row r of a chunk equals a decode of the same cache with
+    context n - L + r + 1 (both GPU paths, against each other and the oracle)."""
+    import torch
+    step = W.make_step("xpath", [300], [90], num_q_heads=16, num_kv_heads=8, head_dim=128, kv_dtype="bf16", seed=95)
+    cache = G.build_cache(step, gpu)
+    out, _ = G.run_chunked(step, cache, gpu)
+    q, cu, tables, ctx = step.chunk_batch()
+    rows = [0, 1, 45, 89]
+    qd = q[rows]
+    ctx_d = np.array([300 - 90 + r + 1 for r in rows], np.int32)
+    tab = np.repeat(tables, len(rows), axis=0)
+    G.announce("decode for cross-path rows")
+    od = G.pkv.paged_attention_decode(G.tensor(qd, "bf16", gpu), cache, G.ints(tab, gpu), G.ints(ctx_d, gpu),
+                                      None, 1, float(step.scale))
+    torch.cuda.synchronize()
+    od = od.cpu().numpy()
+    for i, r in enumerate(rows):
+        assert O.compare(out[r], od[i])["ok"], r
+
+
+def test_chunked_bad_metadata_gives_nan(gpu):
+    """A chunk longer than its context, or than max_q_len, comes out NaN; a
+    block id outside the pool poisons its sequence; the others are exact."""
+    step = W.make_step("badc", [100, 100, 100], [40, 40, 40], num_q_heads=16, num_kv_heads=8, head_dim=128,
+                       kv_dtype="bf16", seed=96)
+    cache = G.build_cache(step, gpu)
+    ro, _ = O.chunked(step, O.pool(step))
+    q, cu, tables, ctx = step.chunk_batch()
+    ctx = ctx.copy()
+    tables = tables.copy()
+    ctx[0] = 30                       # shorter than its 40-row chunk
+    tables[1, 2] = step.num_blocks + 3
+    G.announce("chunked bad metadata")
+    out = G.pkv.paged_attention_chunked(G.tensor(q, "bf16", gpu), G.ints(cu, gpu), 40, cache, G.ints(tables, gpu),
+                                        G.ints(ctx, gpu), float(step.scale)).cpu().numpy()
+    assert np.isnan(out[:80]).all()
+    assert O.compare(out[80:], ro[80:])["ok"]
