@@ -86,6 +86,7 @@ def parse():
     ap.add_argument("--steps-per-graph", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chunked", action="store_true", help="skip the chunked-prefill MFMA measurement")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--workload", default="qwen3_decode", choices=sorted(WORKLOADS),
                     help="the step's shape (default: the Qwen3-0.6B decode step)")
@@ -212,6 +213,88 @@ def time_graphs(fn_per_step, reps, steps, steps_per_graph, warmup):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / 1e3
+
+
+def chunked_flops(step) -> int:
+    """Algorithmic FLOPs of the chunked pass: every unmasked (row, key) pair of
+    every query head costs 2 D for q.k and 2 D for p v."""
+    _, cu, _, ctx = step.chunk_batch()
+    total = 0
+    for i in range(len(ctx)):
+        L, n = int(cu[i + 1] - cu[i]), int(ctx[i])
+        total += L * (n - L) + L * (L + 1) // 2
+    return total * step.num_q_heads * 4 * step.head_dim
+
+
+def measure_chunked(dev, iters: int = 200):
+    """The mixed int8 step: 4 x 512-row causal chunks over a 1536-token cached
+    prefix plus 124 decode rows. Times the chunked (MFMA) pass alone, and the
+    whole step (cache write of 2172 rows, chunked pass, decode pass)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_attention_19_amd as pkv
+    import workloads as W
+    step = W.mixed_int8()
+
+    def dt(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    cache = pkv.KVCache.allocate(step.num_blocks, 8, 128, pkv.I8, dev)
+    pkv.reshape_and_cache(dt(step.prefix_k, "bf16"), dt(step.prefix_v, "bf16"),
+                          dt(step.prefix_slots.astype(np.int64), "i64"), cache)
+    new_k, new_v = dt(step.new_k, "bf16"), dt(step.new_v, "bf16")
+    new_s = dt(step.new_slots.astype(np.int64), "i64")
+    qc, cu, tc, cc = step.chunk_batch()
+    qc, cu, tc, cc = dt(qc, "bf16"), dt(cu, "i32"), dt(tc, "i32"), dt(cc, "i32")
+    max_q = int(np.diff(step.chunk_batch()[1]).max())
+    qd, td, ctxd, nsd = step.decode_batch()
+    max_ns = int(nsd.max())
+    qd, td, ctxd, nsd = dt(qd, "bf16"), dt(td, "i32"), dt(ctxd, "i32"), dt(nsd, "i32")
+    out_c = torch.empty((qc.shape[0], 16, 128), dtype=torch.float32, device=dev)
+    out_d = torch.empty((qd.shape[0], 16, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(256, pkv.decode_workspace_bytes(qd.shape[0], 16, 128, max_ns)), dtype=torch.uint8, device=dev)
+    scale = float(step.scale)
+
+    def chunked():
+        pkv.paged_attention_chunked(qc, cu, max_q, cache, tc, cc, scale, out=out_c)
+
+    def whole():
+        pkv.reshape_and_cache(new_k, new_v, new_s, cache)
+        chunked()
+        pkv.paged_attention_decode(qd, cache, td, ctxd, nsd, max_ns, scale, out=out_d, workspace=ws)
+
+    res = {}
+    for name, fn in (("chunked", chunked), ("step", whole)):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(20):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(max(1, iters // 20)):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) / 1e3 / (max(1, iters // 20) * 20)
+    flops = chunked_flops(step)
+    tflops = flops / res["chunked"] / 1e12
+    return {
+        "workload": "4 x 512-row causal chunks over 1536-token int8 prefixes (16q/8kv/128), "
+                    "plus 124 int8 decode rows in the whole step",
+        "kernel": "chunked_kernel",
+        "chunked_us": round(res["chunked"] * 1e6, 3),
+        "algorithmic_gflop": round(flops / 1e9, 3),
+        "tflops": round(tflops, 2),
+        "mfma_util": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+        "whole_step_us": round(res["step"] * 1e6, 3),
+    }
 
 
 def cpu_baseline(step, seconds):
@@ -358,6 +441,9 @@ def main():
             "traffic": traffic,
         },
     }
+    if not args.no_chunked:
+        log("timing the chunked prefill ...")
+        line["chunked_prefill"] = measure_chunked(dev)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         line["cpu_baseline"] = cpu_baseline(reps[0].step, args.cpu_seconds)

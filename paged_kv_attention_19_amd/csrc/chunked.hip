@@ -69,9 +69,12 @@ template <int KV, int G>
 __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   constexpr int P = kRows / G;               // positions per query tile
   constexpr bool kI8 = (KV == PKV_I8);
+  constexpr float kSlack = 8.0f;
   __shared__ __attribute__((aligned(16))) char s_kv[2][kKBytes + kVBytes];
-  __shared__ float s_ks[2][kTile];
-  __shared__ float s_vs[2][kTile];
+  __shared__ __attribute__((aligned(16))) float s_ks[2][kTile];
+  __shared__ __attribute__((aligned(16))) float s_vs[2][kTile];
+  constexpr int kIdsCached = 1024;          // block ids kept in LDS (16384 tokens)
+  __shared__ int s_ids[kIdsCached];
 
   // ---- work item: (sequence, kv head, query tile), XCD-contiguous ----
   const int QT = (p.max_q_len + P - 1) / P;
@@ -144,10 +147,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 
   // K chunk i: token 16 i + tid / 16, unit tid % 16 (8 dims)
   // V chunk i: token 4 (tid / 16) + i, unit tid % 16
+  // the block ids this tile range needs, read once into LDS (ids past what
+  // LDS holds are read from the table when used)
+  const int nblk_need = min(nblk_seq, ntiles * (kTile / kBlock));
+  for (int j = tid; j < min(nblk_need, kIdsCached); j += kThreads) s_ids[j] = trow[j];
+  __syncthreads();
+
   auto block_of = [&](int tile, int bi, int& id) -> bool {
     const int blk = tile * (kTile / kBlock) + bi;
     if (blk >= nblk_seq) return false;
-    id = trow[blk];
+    id = blk < kIdsCached ? s_ids[blk] : trow[blk];
     if (static_cast<unsigned>(id) >= static_cast<unsigned>(p.num_blocks)) {
       bad = 1;
       return false;
@@ -158,39 +167,52 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   auto gload = [&](int tile) {
     const int u = tid & 15;
     const int t0 = tile * kTile;
+    constexpr int kRowBytes = kI8 ? kD : 2 * kD;
+    // K chunk i sits in block i of the tile; V chunks of this wavefront in block w
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int id = 0;
       const int tok = t0 + 16 * i + (tid >> 4);
       stk[i] = make_uint4(0, 0, 0, 0);
-      if (block_of(tile, i, id) && tok < n) {
-        const size_t row = (static_cast<size_t>(id) * p.num_kv_heads + kh) * kBlock + (tid >> 4);
+      const bool ok = block_of(tile, i, id);
+      id = __builtin_amdgcn_readfirstlane(id);
+      if (ok && tok < n) {
+        const char* base = static_cast<const char*>(p.k) +
+                           (static_cast<size_t>(id) * p.num_kv_heads + kh) * kBlock * kRowBytes;
+        const int off = (tid >> 4) * kRowBytes + u * (kRowBytes / 16);
         if constexpr (kI8) {
-          const uint2 c = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(p.k) + row * kD + 8 * u);
+          const uint2 c = *reinterpret_cast<const uint2*>(base + off);
           stk[i] = make_uint4(c.x, c.y, 0, 0);
         } else {
-          stk[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + row * kD + 8 * u);
+          stk[i] = *reinterpret_cast<const uint4*>(base + off);
         }
       }
     }
     const int tg = tid >> 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    {
       int id = 0;
-      const int tok = t0 + 4 * tg + i;
-      stv[i] = make_uint4(0, 0, 0, 0);
-      if (block_of(tile, tg >> 2, id) && tok < n) {
-        const size_t row = (static_cast<size_t>(id) * p.num_kv_heads + kh) * kBlock + 4 * (tg & 3) + i;
-        if constexpr (kI8) {
-          const uint2 c = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(p.v) + row * kD + 8 * u);
-          stv[i] = make_uint4(c.x, c.y, 0, 0);
-        } else {
-          stv[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + row * kD + 8 * u);
+      const bool ok = block_of(tile, w, id);   // tokens 4 tg .. 4 tg + 3 lie in block tg / 4 == w
+      id = __builtin_amdgcn_readfirstlane(id);
+      const char* base = static_cast<const char*>(p.v) +
+                         (static_cast<size_t>(id) * p.num_kv_heads + kh) * kBlock * kRowBytes;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 4 * tg + i;
+        stv[i] = make_uint4(0, 0, 0, 0);
+        if (ok && tok < n) {
+          const int off = (4 * (tg & 3) + i) * kRowBytes + u * (kRowBytes / 16);
+          if constexpr (kI8) {
+            const uint2 c = *reinterpret_cast<const uint2*>(base + off);
+            stv[i] = make_uint4(c.x, c.y, 0, 0);
+          } else {
+            stv[i] = *reinterpret_cast<const uint4*>(base + off);
+          }
         }
       }
     }
     if constexpr (kI8) {
-      // one scale per token: threads 0..63 fetch the tile's K scales, 64..127 the V scales
+      // one scale per token: threads 0..63 fetch the tile's K scales (pre-multiplied
+      // by the softmax scale), 64..127 the V scales
       sks = 0.f;
       if (tid < 2 * kTile) {
         const int tt = tid & (kTile - 1);
@@ -198,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
         int id = 0;
         if (block_of(tile, tt >> 4, id) && tok < n) {
           const size_t srow = (static_cast<size_t>(id) * p.num_kv_heads + kh) * kBlock + (tt & 15);
-          sks = tid < kTile ? p.k_scale[srow] : p.v_scale[srow];
+          sks = tid < kTile ? p.k_scale[srow] * p.scale_log2 : p.v_scale[srow];
         }
       }
     }
@@ -281,6 +303,26 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       }
     }
 
+    // int8: the scales of this lane's 32 tokens, as runs of 8 (float4 reads)
+    float ksv[2][16], vsv[2][16];
+    if constexpr (kI8) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int t0 = 32 * nb + 8 * h + 16 * half;
+#pragma unroll
+          for (int q4 = 0; q4 < 2; ++q4) {
+            const float4 a = *reinterpret_cast<const float4*>(&s_ks[buf][t0 + 4 * q4]);
+            const float4 b = *reinterpret_cast<const float4*>(&s_vs[buf][t0 + 4 * q4]);
+            const int v0 = 8 * half + 4 * q4;
+            ksv[nb][v0] = a.x; ksv[nb][v0 + 1] = a.y; ksv[nb][v0 + 2] = a.z; ksv[nb][v0 + 3] = a.w;
+            vsv[nb][v0] = b.x; vsv[nb][v0 + 1] = b.y; vsv[nb][v0 + 2] = b.z; vsv[nb][v0 + 3] = b.w;
+          }
+        }
+      }
+    }
+
     // scores: register v of half nb holds token 32 nb + (v % 8) + 8 h + 16 (v / 8) of the tile
     const int tbase = it * kTile;
     const bool diag = it >= first_diag;
@@ -290,43 +332,48 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int tt = 32 * nb + (v & 7) + 8 * h + 16 * (v >> 3);
-        float sv = sacc[nb][v] * p.scale_log2;
-        if constexpr (kI8) sv *= s_ks[buf][tt];
+        float sv;
+        if constexpr (kI8) sv = sacc[nb][v] * ksv[nb][v];   // k scale x softmax scale
+        else sv = sacc[nb][v] * p.scale_log2;
         if (diag && tbase + tt > pos) sv = neg_inf();
         sacc[nb][v] = sv;
         tmax = fmaxf(tmax, sv);
       }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mnew = fmaxf(m, tmax);
-    const float corr = (mnew == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
-    m = mnew;
+    // move the reference max only when the tile exceeds it by more than the
+    // slack: weights stay below 2^kSlack and O is rarely rescaled
+    const bool need = tmax > m + kSlack;
+    if (wave_any(need)) {
+      const float mnew = need ? tmax : m;
+      const float corr = __builtin_amdgcn_exp2f(m - mnew);   // m = -inf -> 0; unchanged -> 1
+      l *= corr;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= corr;
+      m = mnew;
+    }
     const float mu = (m == neg_inf()) ? 0.f : m;
     float rsum = 0.f;
-    uint32_t pb[4][4];   // P^T as bf16: high part
-    uint32_t pl[4][4];   // and the residual p - high, also bf16 (together ~2^-17 relative)
+    bf16x8_t phi[4], plo[4];   // P^T as a bf16 high part and a bf16 residual (~2^-17 together)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        float p0 = __builtin_amdgcn_exp2f(sacc[nb][v] - mu);
-        float p1 = __builtin_amdgcn_exp2f(sacc[nb][v + 1] - mu);
-        rsum += p0 + p1;
-        if constexpr (kI8) {
-          const int tt = 32 * nb + (v & 7) + 8 * h + 16 * (v >> 3);
-          p0 *= s_vs[buf][tt];
-          p1 *= s_vs[buf][tt + 1];
+      for (int half = 0; half < 2; ++half) {
+        // k-step 2 nb + half of the PV product: registers 8 half .. 8 half + 7
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int v = 8 * half + j;
+          float pv = __builtin_amdgcn_exp2f(sacc[nb][v] - mu);
+          rsum += pv;
+          if constexpr (kI8) pv *= vsv[nb][v];
+          const __bf16 hi = static_cast<__bf16>(pv);
+          phi[2 * nb + half][j] = hi;
+          plo[2 * nb + half][j] = static_cast<__bf16>(pv - static_cast<float>(hi));
         }
-        // k-step 2 nb + v / 8 of the PV product, elements (v % 8, v % 8 + 1)
-        const __bf16 h0 = static_cast<__bf16>(p0), h1 = static_cast<__bf16>(p1);
-        pb[2 * nb + (v >> 3)][(v & 7) >> 1] = __builtin_bit_cast(uint32_t, bf16x2_t{h0, h1});
-        pl[2 * nb + (v >> 3)][(v & 7) >> 1] = pack_bf16(p0 - static_cast<float>(h0), p1 - static_cast<float>(h1));
       }
     }
     rsum += __shfl_xor(rsum, 32);
-    l = l * corr + rsum;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] *= corr;
+    l += rsum;
 
     // O^T += V^T P^T
 #pragma unroll
@@ -334,12 +381,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const uint4 a = *reinterpret_cast<const uint4*>(vb + vt_addr(32 * db + (lane & 31), 2 * ks + h));
-        const uint4 bw = make_uint4(pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]);
-        const uint4 bl = make_uint4(pl[ks][0], pl[ks][1], pl[ks][2], pl[ks][3]);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                        __builtin_bit_cast(bf16x8_t, bw), o[db], 0, 0, 0);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                        __builtin_bit_cast(bf16x8_t, bl), o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), phi[ks], o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), plo[ks], o[db], 0, 0, 0);
       }
     }
 
