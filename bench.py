@@ -34,7 +34,8 @@ if ROOT not in sys.path:
 METRIC = "paged-attn decode KV GB/s (% HBM peak) + seq-steps/s; chunked-prefill MFMA util"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
-KERNEL_FILES = ("paged_kv_attention_19_amd/csrc/decode.hip", "paged_kv_attention_19_amd/csrc/pkv_device.h")
+KERNEL_FILES = ("paged_kv_attention_19_amd/csrc/decode_kernel.h", "paged_kv_attention_19_amd/csrc/decode_bf16.hip",
+                "paged_kv_attention_19_amd/csrc/pkv_device.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_qwen3_traffic.json")
 
 
