@@ -8,10 +8,12 @@ sequences, 16 query / 8 KV heads, head_dim 128, bf16 q/K/V from N(0, 1),
 context lengths uniform in [128, 384], 16-token blocks drawn from a 4096-block
 pool. Inputs are resident in HBM before timing starts.
 
-The cache is far smaller than MI355X's 256 MB Infinity Cache would need to
-stay cold, so the timed loop rotates through R independent replicas (own
-pool, own block tables, own values); between two uses of one replica the other
-R - 1 replicas touch well over 256 MB, so every step reads its KV from HBM.
+One step's KV (33.6 MB) would sit in MI355X's 256 MB Infinity Cache if the
+same step were repeated, so the timed loop rotates through R replicas that
+stand for R layers of one model step: they share the batch's block tables,
+context lengths and slots (as an engine's layers do) and each owns its KV pool
+and its q/K/V values. Between two uses of one replica the other R - 1 replicas
+stream well over 256 MB of KV, so every step reads its KV from HBM.
 Steps are launched from HIP graphs (each graph holds many steps) so that host
 launch cost does not pace the GPU.
 
@@ -60,14 +62,18 @@ def kernel_source_hash() -> str:
 
 # name -> (builder(seed, max_tokens_per_split), default replicas, default split size, config text)
 WORKLOADS = {
-    "qwen3_decode": (lambda W, seed, mts, batch: W.qwen3_decode(batch=batch, seed=seed, max_tokens_per_split=mts or None),
+    "qwen3_decode": (lambda W, seed, mts, batch, r: W.qwen3_decode(batch=batch, seed=seed, values_seed=seed + 1000 * r,
+                                                                    max_tokens_per_split=mts or None),
                      16, 0, {"workload": "qwen3_0.6b_layer_decode_step", "context_lens": "uniform[128,384]",
                              "pool_blocks": 4096}),
-    "ragged_decode": (lambda W, seed, mts, batch: W.ragged_decode(seed=seed, max_tokens_per_split=mts or 512),
+    "ragged_decode": (lambda W, seed, mts, batch, r: W.ragged_decode(seed=seed + 1000 * r,
+                                                                      max_tokens_per_split=mts or 512),
                       1, 512, {"workload": "ragged_decode_b256", "context_lens": "log-uniform[64,8192]"}),
-    "long_decode": (lambda W, seed, mts, batch: W.long_decode(seed=seed, num_splits=(32768 // mts) if mts else 64),
+    "long_decode": (lambda W, seed, mts, batch, r: W.long_decode(seed=seed + 1000 * r,
+                                                                  num_splits=(32768 // mts) if mts else 64),
                     1, 512, {"workload": "long_decode_b8_32k", "context_lens": "32768"}),
-    "mixed_int8_decode": (lambda W, seed, mts, batch: W.mixed_int8(seed=seed, max_tokens_per_split=mts or 512),
+    "mixed_int8_decode": (lambda W, seed, mts, batch, r: W.mixed_int8(seed=seed + 1000 * r,
+                                                                       max_tokens_per_split=mts or 512),
                           1, 512, {"workload": "mixed_int8_step_decode_rows", "context_lens": "uniform[256,4096]"}),
 }
 DEFAULT_SEEDS = {"qwen3_decode": 1902, "ragged_decode": 1903, "long_decode": 1904, "mixed_int8_decode": 1905}
@@ -360,7 +366,7 @@ def main():
     t0 = time.time()
     reps = []
     for r in range(args.replicas):
-        step = build(W, seed0 + 1000 * r, args.max_tokens_per_split, args.batch)
+        step = build(W, seed0, args.max_tokens_per_split, args.batch, r)
         reps.append(Replica(step, dev, args.max_tokens_per_split))
     torch.cuda.synchronize()
     log(f"built {len(reps)} replicas in {time.time() - t0:.1f}s; max_ns={[r.max_ns for r in reps][:4]}...")

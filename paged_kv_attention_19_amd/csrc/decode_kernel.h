@@ -179,19 +179,21 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
   auto load_block = [&](int it, Tile& t) {
     const int id = block_id(it);
     const size_t tile = static_cast<size_t>(id) * p.num_kv_heads + kh;
+    // K/V are streamed once per call: non-temporal loads keep them from
+    // evicting the block tables, context lengths and q from the caches
     const char* kt = static_cast<const char*>(p.k) + tile * kTileBytes;  // uniform base
     const char* vt = static_cast<const char*>(p.v) + tile * kTileBytes;
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j)
-        t.k[i][j] = *reinterpret_cast<const uint4*>(kt + lane_off + i * TPI * ROWB + j * LPT * 16);
+        t.k[i][j] = load_nt16(kt + lane_off + i * TPI * ROWB + j * LPT * 16);
     }
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j)
-        t.v[i][j] = *reinterpret_cast<const uint4*>(vt + lane_off + i * TPI * ROWB + j * LPT * 16);
+        t.v[i][j] = load_nt16(vt + lane_off + i * TPI * ROWB + j * LPT * 16);
     }
     if constexpr (kI8) {
 #pragma unroll

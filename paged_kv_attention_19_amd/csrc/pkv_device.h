@@ -15,6 +15,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal (streamed data that should not displace
+// what the caches hold for later use).
+__device__ __forceinline__ uint4 load_nt16(const void* ptr) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(ptr));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // ---- element decoding ------------------------------------------------------
 

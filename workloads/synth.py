@@ -132,8 +132,15 @@ def make_step(name: str, context_lens, q_lens, *, num_q_heads: int, num_kv_heads
               q_dtype: str = BF16, kv_dtype: str = BF16, src_dtype: str | None = None,
               num_splits=None, seed: int = 0, outlier_frac: float = 0.0,
               outlier_mult: float = 8.0, scale: float | None = None,
-              max_blocks_per_seq: int | None = None, threads: int | None = None) -> Step:
-    """Build a step for arbitrary sequences (see the module docstring)."""
+              max_blocks_per_seq: int | None = None, threads: int | None = None,
+              values_seed: int | None = None) -> Step:
+    """Build a step for arbitrary sequences (see the module docstring).
+
+    ``values_seed`` (default ``seed``) seeds the per-sequence value streams
+    alone: steps that share ``seed`` and differ in ``values_seed`` have the same
+    context lengths, block tables and slots but their own q/K/V -- the layers
+    of one model step, which share the batch's block tables and each own a
+    KV pool."""
     ctx = np.asarray(context_lens, np.int64)
     ql = np.asarray(q_lens, np.int64)
     S = len(ctx)
@@ -154,7 +161,7 @@ def make_step(name: str, context_lens, q_lens, *, num_q_heads: int, num_kv_heads
         tables[i, :nblk[i]] = perm[pos:pos + nblk[i]]
         pos += nblk[i]
 
-    kids = ss.spawn(S)
+    kids = (ss if values_seed is None else np.random.SeedSequence(values_seed)).spawn(S)
     nthreads = threads or min(16, os.cpu_count() or 1)
     args = [(kids[i], int(ctx[i]), int(ql[i]), Hq, Hkv, D, outlier_frac, outlier_mult) for i in range(S)]
     if S > 4 and nthreads > 1:
@@ -223,7 +230,7 @@ def tiny_decode(num_splits: int = 1, seed: int = 1901) -> Step:
 
 
 def qwen3_decode(batch: int = 32, num_splits=None, max_tokens_per_split: int | None = None,
-                 seed: int = 1902, num_blocks: int = 4096) -> Step:
+                 seed: int = 1902, num_blocks: int = 4096, values_seed: int | None = None) -> Step:
     """Qwen3-0.6B-shaped single-layer decode step: 16 q / 8 kv heads, D=128,
     bf16 N(0,1), n uniform in [128, 384] (128-token prompt + up to 256 new),
     bs=16, tables from a permutation of a 4096-block pool; the step writes one
@@ -233,7 +240,8 @@ def qwen3_decode(batch: int = 32, num_splits=None, max_tokens_per_split: int | N
     if num_splits is None and max_tokens_per_split is not None:
         num_splits = splits_for(ctx, max_tokens_per_split)
     return make_step("qwen3_decode", ctx, np.ones(batch, np.int64), num_q_heads=16, num_kv_heads=8,
-                     head_dim=128, num_blocks=num_blocks, num_splits=num_splits, seed=seed)
+                     head_dim=128, num_blocks=num_blocks, num_splits=num_splits, seed=seed,
+                     values_seed=values_seed)
 
 
 def ragged_decode(batch: int = 256, max_tokens_per_split: int = 512, seed: int = 1903,
