@@ -36,8 +36,8 @@ if ROOT not in sys.path:
 METRIC = "paged-attn decode KV GB/s (% HBM peak) + seq-steps/s; chunked-prefill MFMA util"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
-KERNEL_FILES = ("paged_kv_attention_19_amd/csrc/decode_kernel.h", "paged_kv_attention_19_amd/csrc/decode_bf16.hip",
-                "paged_kv_attention_19_amd/csrc/pkv_device.h")
+KERNEL_FILES = ("paged_kv_attention_19_amd/csrc/decode_kernel.h", "paged_kv_attention_19_amd/csrc/decode_core.h",
+                "paged_kv_attention_19_amd/csrc/decode_bf16.hip", "paged_kv_attention_19_amd/csrc/pkv_device.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_qwen3_traffic.json")
 
 
@@ -77,6 +77,11 @@ WORKLOADS = {
                           1, 512, {"workload": "mixed_int8_step_decode_rows", "context_lens": "uniform[256,4096]"}),
 }
 DEFAULT_SEEDS = {"qwen3_decode": 1902, "ragged_decode": 1903, "long_decode": 1904, "mixed_int8_decode": 1905}
+# Decode mode measured fastest on MI355X per shape: the small Qwen3 step and
+# the uniform long contexts keep one workgroup per (split, kv head) and merge
+# in LDS; the ragged and int8 batches gain from the balanced deal of tiles.
+DEFAULT_MODES = {"qwen3_decode": "splits", "ragged_decode": "balanced", "long_decode": "splits",
+                 "mixed_int8_decode": "balanced"}
 
 
 def parse():
@@ -97,6 +102,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--workload", default="qwen3_decode", choices=sorted(WORKLOADS),
                     help="the step's shape (default: the Qwen3-0.6B decode step)")
+    ap.add_argument("--decode-mode", choices=("balanced", "splits"), default=None,
+                    help="balanced: the library deals the batch's tiles evenly over the GPU and merges cut "
+                         "sequences in the same launch (max_num_splits = 0); splits: caller-chosen "
+                         "num_splits (from --max-tokens-per-split) with a separate merge pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 8 times (to scale HBM counters)")
     return ap.parse_args()
@@ -118,7 +127,7 @@ def copy_calibration(nbytes: int) -> None:
 class Replica:
     """One independent copy of the workload, resident on the GPU."""
 
-    def __init__(self, step, dev, max_tokens_per_split):
+    def __init__(self, step, dev, max_tokens_per_split, balanced=False):
         import numpy as np
         import torch
 
@@ -138,8 +147,9 @@ class Replica:
         self.q = dt(q, step.q_dtype)
         self.tables = dt(tables.astype(np.int32), "i32")
         self.ctx = dt(ctx.astype(np.int32), "i32")
-        self.max_ns = int(ns.max())
-        self.ns = dt(ns.astype(np.int32), "i32")
+        self.balanced = balanced
+        self.max_ns = 0 if balanced else int(ns.max())
+        self.ns = None if balanced else dt(ns.astype(np.int32), "i32")
         # the step's new rows: one per decode sequence (chunk rows belong to the chunked pass)
         dec_rows = np.concatenate([np.arange(step.cu_q_lens[i], step.cu_q_lens[i + 1]) for i in step.decode_idx])
         self.new_k = dt(step.new_k[dec_rows], step.src_dtype)
@@ -149,7 +159,7 @@ class Replica:
         self.out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
         self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
         wsb = pkv.decode_workspace_bytes(B, Hq, D, self.max_ns)
-        self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device=dev)   # balanced counters start at 0
         S = self.max_ns
         if S > 1:
             flat = self.ws.view(torch.float32)
@@ -171,7 +181,7 @@ class Replica:
 
     def partials(self):
         import paged_kv_attention_19_amd as pkv
-        if self.max_ns == 1:
+        if self.max_ns <= 1:
             self.decode()
         else:
             pkv.paged_attention_decode(self.q, self.cache, self.tables, self.ctx, self.ns, self.max_ns,
@@ -179,7 +189,7 @@ class Replica:
 
     def combine(self):
         import paged_kv_attention_19_amd as pkv
-        if self.max_ns == 1:
+        if self.max_ns <= 1:
             return
         pkv.lse_combine(self.o_part, self.lse_part, self.ns, out=self.out, out_lse=self.lse)
 
@@ -257,12 +267,12 @@ def measure_chunked(dev, iters: int = 200):
     qc, cu, tc, cc = step.chunk_batch()
     qc, cu, tc, cc = dt(qc, "bf16"), dt(cu, "i32"), dt(tc, "i32"), dt(cc, "i32")
     max_q = int(np.diff(step.chunk_batch()[1]).max())
-    qd, td, ctxd, nsd = step.decode_batch()
-    max_ns = int(nsd.max())
-    qd, td, ctxd, nsd = dt(qd, "bf16"), dt(td, "i32"), dt(ctxd, "i32"), dt(nsd, "i32")
+    qd, td, ctxd, _ = step.decode_batch()
+    max_ns = 0   # the decode rows use the balanced mode
+    qd, td, ctxd = dt(qd, "bf16"), dt(td, "i32"), dt(ctxd, "i32")
     out_c = torch.empty((qc.shape[0], 16, 128), dtype=torch.float32, device=dev)
     out_d = torch.empty((qd.shape[0], 16, 128), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(256, pkv.decode_workspace_bytes(qd.shape[0], 16, 128, max_ns)), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(256, pkv.decode_workspace_bytes(qd.shape[0], 16, 128, max_ns)), dtype=torch.uint8, device=dev)
     scale = float(step.scale)
 
     def chunked():
@@ -271,7 +281,7 @@ def measure_chunked(dev, iters: int = 200):
     def whole():
         pkv.reshape_and_cache(new_k, new_v, new_s, cache)
         chunked()
-        pkv.paged_attention_decode(qd, cache, td, ctxd, nsd, max_ns, scale, out=out_d, workspace=ws)
+        pkv.paged_attention_decode(qd, cache, td, ctxd, None, max_ns, scale, out=out_d, workspace=ws)
 
     res = {}
     for name, fn in (("chunked", chunked), ("step", whole)):
@@ -358,6 +368,8 @@ def main():
     dev = torch.device("cuda:0")
     pkv.lib()
     build, default_reps, default_mts, cfg_text = WORKLOADS[args.workload]
+    if args.decode_mode is None:
+        args.decode_mode = DEFAULT_MODES[args.workload]
     if args.max_tokens_per_split is None:
         args.max_tokens_per_split = default_mts
     if args.replicas is None:
@@ -367,7 +379,7 @@ def main():
     reps = []
     for r in range(args.replicas):
         step = build(W, seed0, args.max_tokens_per_split, args.batch, r)
-        reps.append(Replica(step, dev, args.max_tokens_per_split))
+        reps.append(Replica(step, dev, args.max_tokens_per_split, balanced=args.decode_mode == "balanced"))
     torch.cuda.synchronize()
     log(f"built {len(reps)} replicas in {time.time() - t0:.1f}s; max_ns={[r.max_ns for r in reps][:4]}...")
 
@@ -396,20 +408,22 @@ def main():
     per_kernel = {}
     n_k = min(steps, 4096)
     sec_p = time_graphs(lambda r: r.partials(), reps, n_k, args.steps_per_graph, 64)
-    per_kernel["decode_partial"] = sec_p / n_k
+    dom = "decode_balanced" if reps[0].balanced else "decode_partial"
+    per_kernel[dom] = sec_p / n_k
     if reps[0].max_ns > 1:
         sec_c = time_graphs(lambda r: r.combine(), reps, n_k, args.steps_per_graph, 64)
         per_kernel["lse_combine"] = sec_c / n_k
     sec_r = time_graphs(lambda r: r.reshape(), reps, n_k, args.steps_per_graph, 64)
     per_kernel["reshape_and_cache"] = sec_r / n_k
     partial_bytes = sum(reps[i % R].kv_bytes for i in range(n_k)) / n_k
-    achieved = partial_bytes / per_kernel["decode_partial"] / 1e9
+    achieved = partial_bytes / per_kernel[dom] / 1e9
 
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if (tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == args.workload
+                and tr.get("decode_mode") == args.decode_mode
                 and tr.get("max_tokens_per_split") == args.max_tokens_per_split):
             traffic = tr.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
@@ -431,7 +445,8 @@ def main():
         "config": dict(cfg_text, **{
             "batch": reps[0].batch,
             "num_q_heads": 16, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
-            "max_tokens_per_split": args.max_tokens_per_split,
+            "decode_mode": args.decode_mode,
+            "max_tokens_per_split": None if reps[0].balanced else args.max_tokens_per_split,
             "replicas": R, "kv_bytes_per_step": int(kv_total / steps),
             "parallelism": "none",
         }),
@@ -440,7 +455,7 @@ def main():
         "kernel_us": {k: round(v * 1e6, 3) for k, v in per_kernel.items()},
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_partial_kernel",
+            "kernel": "decode_balanced_kernel" if reps[0].balanced else "decode_partial_kernel",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -107,6 +107,12 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, int32_t s
 
 /*
  * Bytes of device workspace pkv_paged_attention_decode needs:
+ *   max_num_splits == 0 : the balanced mode's arrival counters (batch *
+ *                         num_q_heads int32, rounded up to 256) followed by
+ *                         its partial slots (2048 x 2 x num_q_heads x
+ *                         (head_dim + 1) float32). The counters must be zero
+ *                         before the first call on a workspace; every call
+ *                         leaves them zero.
  *   max_num_splits == 1 : 0 (the partial pass writes `out` directly);
  *   otherwise           : batch * max_num_splits * num_q_heads * (head_dim + 1) * 4,
  *                         rounded up to 256. Layout: o_part float32
@@ -129,6 +135,12 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t he
  *                  sequence b covers tokens [s*tps, min(n_b, (s+1)*tps)) with
  *                  tps = block_size * ceil(ceil(n_b / ns_b) / block_size);
  *                  every choice gives the same result up to rounding.
+ *                  max_num_splits == 0 (num_splits NULL) selects the balanced
+ *                  mode: the library deals the batch's (sequence, kv head,
+ *                  block) tiles to the GPU's wavefronts in equal contiguous
+ *                  ranges and merges cut sequences within the same launch, so
+ *                  the split is chosen by the data, not the caller. Calls that
+ *                  share a workspace must not overlap (one stream is fine).
  *   scale        : multiplies q . k before the softmax.
  *   out          : float32 [batch][num_q_heads][head_dim]:
  *                  sum_t softmax_t(scale * q . k_t) v_t over t < n_b.

@@ -223,6 +223,10 @@ def paged_attention_decode(q: torch.Tensor, cache: KVCache, block_tables: torch.
                            return_lse: bool = False, partials_only: bool = False):
     """Decode attention: ``q [B][Hq][D]`` -> ``out [B][Hq][D]`` float32 (and lse).
 
+    ``max_num_splits=0`` with ``num_splits=None`` selects the balanced mode; a
+    workspace passed for it must have been zero-filled once (every call
+    leaves its counters at zero).
+
     ``partials_only=True`` (needs ``max_num_splits > 1`` and a ``workspace``)
     runs only the split pass and returns ``(o_part [B][S][Hq][D],
     lse_part [B][S][Hq])`` views of the workspace, for :func:`lse_combine`."""
@@ -264,7 +268,8 @@ def paged_attention_decode(q: torch.Tensor, cache: KVCache, block_tables: torch.
         _need(out_lse, "out_lse", (torch.float32,), 2)
     need = decode_workspace_bytes(B, Hq, D, max_num_splits)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zero-filled: the balanced mode's arrival counters must start at 0
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     d = cache.descriptor()
     _check(lib().pkv_paged_attention_decode(

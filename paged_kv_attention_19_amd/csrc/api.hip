@@ -94,6 +94,33 @@ int decode_waves(int /*max_blocks_per_seq*/, int /*max_num_splits*/) {
   return forced ? forced : 4;
 }
 
+// Deep prefetch (5 blocks in flight per wavefront) when the whole grid fits
+// the chip's 256 CUs in one pass: each wavefront then runs alone on its SIMD,
+// registers are plentiful, and only its own loads in flight hide latency.
+// PKV_DECODE_PREFETCH=deep|shallow overrides, for tuning.
+bool decode_deep(int batch, int max_num_splits, int num_kv_heads, int waves) {
+  static const int forced = [] {
+    const char* e = std::getenv("PKV_DECODE_PREFETCH");
+    if (e == nullptr) return 0;
+    return std::string(e) == "deep" ? 1 : (std::string(e) == "shallow" ? 2 : 0);
+  }();
+  if (waves != 4) return false;
+  if (forced) return forced == 1;
+  return static_cast<int64_t>(batch) * max_num_splits * num_kv_heads <= 256;
+}
+
+// Balanced decode: 4 wavefronts per workgroup, 256 workgroups (one per CU)
+// or 512 for large batches; each wavefront owns two partial slots of
+// G (D + 1) floats (G <= Hq).
+constexpr int kBalancedMaxWorkgroups = 512;
+size_t balanced_part_bytes(int num_q_heads, int head_dim) {
+  return static_cast<size_t>(kBalancedMaxWorkgroups) * 4 * 2 * num_q_heads * (head_dim + 1) * sizeof(float);
+}
+int balanced_workgroups(int batch, int num_kv_heads, int max_blocks) {
+  const int64_t tiles_bound = static_cast<int64_t>(batch) * num_kv_heads * max_blocks;
+  return tiles_bound <= 65536 ? 256 : kBalancedMaxWorkgroups;
+}
+
 }  // namespace
 
 extern "C" {
@@ -139,7 +166,11 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, int32_t s
 }
 
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t max_num_splits) {
-  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_num_splits <= 0) return 0;
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_num_splits < 0) return 0;
+  if (max_num_splits == 0) {
+    const size_t counters = (static_cast<size_t>(batch) * num_q_heads * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
+    return counters + balanced_part_bytes(num_q_heads, head_dim);
+  }
   if (max_num_splits == 1) return 0;
   const size_t rows = static_cast<size_t>(batch) * max_num_splits * num_q_heads;
   const size_t bytes = rows * (static_cast<size_t>(head_dim) + 1) * sizeof(float);
@@ -165,10 +196,16 @@ pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t ba
     return fail(PKV_ERR_INVALID_ARG, "%s: out is NULL (partials-only mode needs max_num_splits > 1)", fn);
   if (!aligned16(q) || !aligned16(out)) return fail(PKV_ERR_INVALID_ARG, "%s: q/out not 16-byte aligned", fn);
   if (max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "%s: max_blocks_per_seq=%d", fn, max_blocks_per_seq);
-  if (max_num_splits < 1 || max_num_splits > 65535)
-    return fail(PKV_ERR_INVALID_ARG, "%s: max_num_splits=%d (1..65535)", fn, max_num_splits);
+  const bool balanced = max_num_splits == 0;
+  if (max_num_splits < 0 || max_num_splits > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "%s: max_num_splits=%d (0..65535)", fn, max_num_splits);
   if (max_num_splits > 1 && num_splits == nullptr)
     return fail(PKV_ERR_INVALID_ARG, "%s: num_splits is NULL with max_num_splits=%d", fn, max_num_splits);
+  if (balanced && num_splits != nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "%s: max_num_splits=0 (balanced) takes no num_splits", fn);
+  if (balanced && out == nullptr) return fail(PKV_ERR_INVALID_ARG, "%s: out is NULL in balanced mode", fn);
+  if (balanced && static_cast<int64_t>(batch) * cache->num_kv_heads * max_blocks_per_seq > (int64_t(1) << 40))
+    return fail(PKV_ERR_UNSUPPORTED, "%s: batch too large for the balanced mode", fn);
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "%s: scale is not finite", fn);
   const int D = cache->head_dim;
   const size_t need = pkv_decode_workspace_bytes(batch, num_q_heads, D, max_num_splits);
@@ -178,6 +215,39 @@ pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t ba
   if (need > 0 && !aligned16(workspace)) return fail(PKV_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int group = num_q_heads / cache->num_kv_heads;
+  if (balanced) {
+    pkv::DecodeParams p{};
+    p.q = q;
+    p.k = cache->k;
+    p.v = cache->v;
+    p.k_scale = cache->k_scale;
+    p.v_scale = cache->v_scale;
+    p.tables = block_tables;
+    p.ctx = context_lens;
+    p.o = out;
+    p.lse = out_lse;
+    p.batch = batch;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = cache->num_kv_heads;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = cache->num_blocks;
+    p.max_ns = 0;
+    p.direct = 1;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.counters = static_cast<int32_t*>(workspace);
+    const size_t counters = (static_cast<size_t>(batch) * num_q_heads * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
+    p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + counters);
+    const int wgs = balanced_workgroups(batch, cache->num_kv_heads, max_blocks_per_seq);
+    hipError_t e;
+    switch (cache->kv_dtype) {
+      case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, -wgs, false, st); break;
+      case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, -wgs, false, st); break;
+      default: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, -wgs, false, st); break;
+    }
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+  }
   const bool direct = max_num_splits == 1;
   float* o_part = static_cast<float*>(workspace);
   float* lse_part = direct ? nullptr : o_part + static_cast<size_t>(batch) * max_num_splits * num_q_heads * D;
@@ -201,13 +271,13 @@ pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t ba
   p.direct = direct ? 1 : 0;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.batch = batch;
-  const int group = num_q_heads / cache->num_kv_heads;
   const int waves = decode_waves(max_blocks_per_seq, max_num_splits);
+  const bool deep = decode_deep(batch, max_num_splits, cache->num_kv_heads, waves);
   hipError_t e;
   switch (cache->kv_dtype) {
-    case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, waves, st); break;
-    case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, waves, st); break;
-    default: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, waves, st); break;
+    case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, waves, deep, st); break;
+    case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, waves, deep, st); break;
+    default: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, waves, deep, st); break;
   }
   if (e != hipSuccess) return hip_fail(e, fn);
   if (!direct && out != nullptr) {

@@ -1,0 +1,259 @@
+// Per-wavefront decode machinery shared by the split-K and the balanced
+// decode kernels: the lane layout of a KV tile, the loads, the QK / online
+// softmax / PV update of one 16-token block, and the merges of a wavefront's
+// token slots.
+//
+// Lane layout. A (block, kv head) K tile -- 16 rows of head_dim elements --
+// is contiguous in HBM. A wavefront reads it with 16-byte loads in which LPT
+// consecutive lanes cover a contiguous 16*LPT-byte run of one token row (128
+// bytes, a whole cache line, for bf16 head_dim 128) and each lane holds CPL
+// such chunks of its row; one load group covers TPI = 64 / LPT tokens. The V
+// tile is read the same way. The tile stays in registers and serves all G
+// query heads of the GQA group, so every KV byte is read from HBM once. A
+// lane's partial q.k is reduced over its LPT lanes with DPP moves; each of the
+// TPI token slots keeps its own running max / sum / accumulator (base-2
+// exponentials). The running max is only moved when a block's max exceeds it
+// by more than kRescaleSlack (weights then stay below 2^kRescaleSlack), which
+// spares the accumulator rescale on almost every block; the result is the
+// same softmax, normalised by the same reference.
+#pragma once
+
+#include <type_traits>
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+
+template <int KV, int QT, int D, int G>
+struct WaveDecoder {
+  using Geo = KvGeom<KV>;
+  static constexpr int EPL = Geo::kEpl;                 // elements per 16-byte chunk
+  static constexpr int ROWB = D * Geo::kEsize;          // bytes per token row
+  static constexpr int ROWC = ROWB / 16;                // chunks per token row
+  static constexpr int CPL = ROWC >= 16 ? 2 : 1;        // chunks of a row per lane
+  static constexpr int LPT = ROWC / CPL;                // lanes per token row
+  static constexpr int TPI = kWave / LPT;               // tokens per load group
+  static constexpr int IPB = kBlock / TPI;              // load groups per block tile
+  static constexpr int NE = CPL * EPL;                  // row elements per lane
+  static constexpr int kTileBytes = kBlock * ROWB;
+  static constexpr bool kDot2 = (KV == PKV_BF16 && QT == PKV_BF16);
+  static constexpr bool kI8 = (KV == PKV_I8);
+  static constexpr float kRescaleSlack = 8.0f;
+  static_assert(TPI * LPT == kWave && IPB * TPI == kBlock && IPB * CPL * 1024 == kTileBytes, "geometry");
+
+  struct Tile {
+    uint4 k[IPB][CPL];
+    uint4 v[IPB][CPL];
+    float ks[IPB];
+    float vs[IPB];
+  };
+
+  int lane, tslot, lc, lane_off;
+  float qf[G][NE];
+  uint32_t q2[G][NE / 2];
+  float m[G], l[G], acc[G][NE];
+
+  __device__ __forceinline__ void init_lane() {
+    lane = threadIdx.x & 63;
+    tslot = lane / LPT;
+    lc = lane % LPT;
+    lane_off = tslot * ROWB + lc * 16;   // byte offset of the lane's first chunk in a tile
+  }
+
+  // The G query rows of group kh of sequence b, on the lane's NE dims.
+  __device__ __forceinline__ void load_q(const void* q, int num_q_heads, int b, int h0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const size_t base = (static_cast<size_t>(b) * num_q_heads + h0 + g) * D + (j * LPT + lc) * EPL;
+        if constexpr (kDot2) {
+          const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + base);
+          q2[g][4 * j + 0] = x.x;
+          q2[g][4 * j + 1] = x.y;
+          q2[g][4 * j + 2] = x.z;
+          q2[g][4 * j + 3] = x.w;
+        } else if constexpr (QT == PKV_BF16) {
+          const uint16_t* qp = static_cast<const uint16_t*>(q) + base;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) qf[g][j * EPL + e] = __uint_as_float(static_cast<uint32_t>(qp[e]) << 16);
+        } else {
+          const float* qp = static_cast<const float*>(q) + base;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) qf[g][j * EPL + e] = qp[e];
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = neg_inf();
+      l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) acc[g][e] = 0.f;
+    }
+  }
+
+  // Loads of the (block id, kv head) tile; id must already be a valid block.
+  __device__ __forceinline__ void load_tile(const DecodeParams& p, int id, int kh, Tile& t) const {
+    const size_t tile = static_cast<size_t>(id) * p.num_kv_heads + kh;
+    // K/V are streamed once per call: non-temporal loads keep them from
+    // evicting the block tables, context lengths and q from the caches
+    const char* kt = static_cast<const char*>(p.k) + tile * kTileBytes;  // uniform base
+    const char* vt = static_cast<const char*>(p.v) + tile * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) t.k[i][j] = load_nt16(kt + lane_off + i * TPI * ROWB + j * LPT * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) t.v[i][j] = load_nt16(vt + lane_off + i * TPI * ROWB + j * LPT * 16);
+    }
+    if constexpr (kI8) {
+#pragma unroll
+      for (int i = 0; i < IPB; ++i) {
+        t.ks[i] = p.k_scale[tile * kBlock + i * TPI + tslot];
+        t.vs[i] = p.v_scale[tile * kBlock + i * TPI + tslot];
+      }
+    }
+  }
+
+  // One block: tokens tok0 .. tok0 + 15; tokens >= t1 are masked (tail).
+  template <bool kFull>
+  __device__ __forceinline__ void process(const Tile& t, int tok0, int t1, float scale_log2) {
+    float sc[IPB][G];
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      float kf[NE];
+      if constexpr (!kDot2) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) unpack16<KV>(t.k[i][j], kf + j * EPL);
+      }
+      const bool valid = kFull || (tok0 + i * TPI + tslot < t1);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float d = 0.f;
+        if constexpr (kDot2) {
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) {
+            const uint32_t kw[4] = {t.k[i][j].x, t.k[i][j].y, t.k[i][j].z, t.k[i][j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q2[g][4 * j + e]),
+                                                  __builtin_bit_cast(bf16x2_t, kw[e]), d, false);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < NE; ++e) d = fmaf(qf[g][e], kf[e], d);
+        }
+        d = group_sum<LPT>(d);
+        if constexpr (kI8) d *= t.ks[i] * scale_log2;
+        else d *= scale_log2;
+        if constexpr (!kFull) d = valid ? d : neg_inf();
+        sc[i][g] = d;
+      }
+    }
+    // online softmax: move the reference max only when a block exceeds it by
+    // more than the slack (or the slot had no finite score yet)
+    bool need = false;
+    float bm[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      bm[g] = sc[0][g];
+#pragma unroll
+      for (int i = 1; i < IPB; ++i) bm[g] = fmaxf(bm[g], sc[i][g]);
+      need = need || (bm[g] > m[g] + kRescaleSlack);
+    }
+    if (wave_any(need)) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (bm[g] > m[g] + kRescaleSlack) {
+          const float corr = __builtin_amdgcn_exp2f(m[g] - bm[g]);  // m = -inf -> 0
+          l[g] *= corr;
+#pragma unroll
+          for (int e = 0; e < NE; ++e) acc[g][e] *= corr;
+          m[g] = bm[g];
+        }
+      }
+    }
+    float pr[IPB][G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mu = (m[g] == neg_inf()) ? 0.f : m[g];
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < IPB; ++i) {
+        pr[i][g] = __builtin_amdgcn_exp2f(sc[i][g] - mu);  // -inf -> 0
+        sum += pr[i][g];
+      }
+      l[g] += sum;
+    }
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      float vf[NE];
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) unpack16<KV>(t.v[i][j], vf + j * EPL);
+      // rows past the context (and their int8 scales) may hold NaN: masked
+      // tokens contribute by select, never as 0 * NaN
+      const bool valid = kFull || (tok0 + i * TPI + tslot < t1);
+      if constexpr (!kFull) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) vf[e] = valid ? vf[e] : 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float pw = pr[i][g];
+        if constexpr (kI8) pw = (kFull || valid) ? pw * t.vs[i] : 0.f;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[g][e] = fmaf(pw, vf[e], acc[g][e]);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void run(const Tile& t, int tok0, int t1, float scale_log2) {
+    if (tok0 + kBlock <= t1) process<true>(t, tok0, t1, scale_log2);
+    else process<false>(t, tok0, t1, scale_log2);
+  }
+
+  // Bring the token slots to the wavefront's common reference max M.
+  __device__ __forceinline__ void slots_to_common_max(float (&M)[G]) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mm = m[g];
+#pragma unroll
+      for (int msk = LPT; msk < kWave; msk <<= 1) mm = fmaxf(mm, __shfl_xor(mm, msk));
+      M[g] = mm;
+      const float a = (m[g] == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(m[g] - mm);
+      l[g] *= a;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) acc[g][e] *= a;
+      m[g] = mm;
+    }
+  }
+
+  // After slots_to_common_max: sum the slots, so every slot holds the
+  // wavefront's total (l and acc); lanes 0 .. LPT-1 then hold all D dims.
+  __device__ __forceinline__ void sum_slots() {
+#pragma unroll
+    for (int msk = LPT; msk < kWave; msk <<= 1) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        l[g] += __shfl_xor(l[g], msk);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[g][e] += __shfl_xor(acc[g][e], msk);
+      }
+    }
+  }
+
+  // Dimension of element e of the lane's row chunk j.
+  __device__ __forceinline__ int dim_of(int j, int e) const { return (j * LPT + lc) * EPL + e; }
+};
+
+}  // namespace pkv

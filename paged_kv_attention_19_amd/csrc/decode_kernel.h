@@ -1,57 +1,36 @@
-// Split-K paged decode, partial pass: the kernel template. Instantiated per
-// KV element type in decode_f32.hip, decode_bf16.hip and decode_i8.hip.
+// Decode kernels for gfx950: the split-K partial pass and the balanced
+// single-launch decode. Instantiated per KV element type in decode_f32.hip,
+// decode_bf16.hip and decode_i8.hip.
 //
 // What is computed (course README "Build an LLM Inference Engine From
 // Scratch", curriculum S06 PagedAttention and S12 FlashAttention; claims s06
 // and s12 in section "The code asserts its own claims"): for every sequence b
 // and query head h, softmax(scale * q_h . k_t) weighted values over the
-// sequence's tokens t < n_b, the K/V rows read through the block table. The
-// tokens are cut into num_splits[b] block-aligned ranges; each range is
-// reduced with an online softmax to (o_s, lse_s), and the ranges are merged by
-// log-sum-exp.
+// sequence's tokens t < n_b, the K/V rows read through the block table.
 //
-// Work mapping. One workgroup of NW wavefronts per (split, kv head, sequence).
-// The split's 16-token blocks are dealt to the wavefronts round-robin. A
-// (block, kv head) K tile -- 16 rows of head_dim elements -- is contiguous in
-// HBM; a wavefront reads it with 16-byte loads in which LPT consecutive lanes
-// cover a contiguous 16*LPT-byte run of one token row (128 bytes, a whole
-// cache line, for bf16 head_dim 128) and each lane holds CPL such chunks of
-// its row. The V tile is read the same way. The tile stays in registers and
-// serves all G query heads of the GQA group, so every KV byte is read from
-// HBM once. A lane's partial q.k is reduced over its LPT lanes with DPP moves;
-// each of the TPI token slots of a wavefront keeps its own running max / sum /
-// accumulator (base-2 exponentials), merged across slots with lane shuffles
-// and across wavefronts through LDS at the end. The running max is only moved
-// when a block's max exceeds it by more than kRescaleSlack (weights then stay
-// below 2^kRescaleSlack), which spares the accumulator rescale on almost every
-// block; the result is the same softmax, normalised by the same reference.
+// Split-K: the tokens are cut into num_splits[b] block-aligned ranges; one
+// workgroup of NW wavefronts reduces each (split, kv head, sequence) with an
+// online softmax to (o_s, lse_s), and the ranges are merged by log-sum-exp.
+//
+// Balanced: the (sequence, kv head, block) tiles of the whole batch, in that
+// order, are dealt to the wavefronts of the grid in equal contiguous ranges,
+// so every CU streams the same number of KV bytes whatever the context
+// lengths. A (sequence, kv head) segment that falls inside one range is
+// written directly; one that a range boundary cuts leaves a partial per
+// contributing wavefront (agent-coherent stores), and the last contributor to
+// finish (a device-atomic arrival counter) merges them by log-sum-exp, in the
+// same launch.
 #pragma once
 
-#include <type_traits>
-
-#include "pkv_device.h"
-#include "pkv_launch.h"
+#include "decode_core.h"
 
 namespace pkv {
 
-constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
-
-template <int KV, int QT, int D, int G, int NW>
+template <int KV, int QT, int D, int G, int NW, int PD>
 __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p) {
-  using Geo = KvGeom<KV>;
-  constexpr int EPL = Geo::kEpl;                   // elements per 16-byte chunk
-  constexpr int ROWB = D * Geo::kEsize;            // bytes per token row
-  constexpr int ROWC = ROWB / 16;                  // chunks per token row
-  constexpr int CPL = ROWC >= 16 ? 2 : 1;          // chunks of a row per lane
-  constexpr int LPT = ROWC / CPL;                  // lanes per token row
-  constexpr int TPI = kWave / LPT;                 // tokens per load group
-  constexpr int IPB = kBlock / TPI;                // load groups per block tile
-  constexpr int NE = CPL * EPL;                    // row elements per lane
-  constexpr int kTileBytes = kBlock * ROWB;
-  constexpr bool kDot2 = (KV == PKV_BF16 && QT == PKV_BF16);
-  constexpr bool kI8 = (KV == PKV_I8);
-  constexpr float kRescaleSlack = 8.0f;
-  static_assert(TPI * LPT == kWave && IPB * TPI == kBlock && IPB * CPL * 1024 == kTileBytes, "geometry");
+  using WD = WaveDecoder<KV, QT, D, G>;
+  using Tile = typename WD::Tile;
+  constexpr int LPT = WD::LPT, TPI = WD::TPI, CPL = WD::CPL, EPL = WD::EPL;
 
   // cross-slot merge through LDS when the (wave, slot) states fit in 64 KiB
   constexpr bool kLdsMerge = NW * TPI * G * D * 4 <= 65536;
@@ -72,38 +51,13 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
   const int kh = item % p.num_kv_heads;
   const int s = (item / p.num_kv_heads) % S;
   const int b = item / (p.num_kv_heads * S);
-  const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tslot = lane / LPT;
-  const int lc = lane % LPT;
-  const int lane_off = tslot * ROWB + lc * 16;     // byte offset of the lane's first chunk in a tile
 
-  // ---- the G query rows of this group, on the lane's NE dims ----
+  WD wd;
+  wd.init_lane();
+  const int lane = wd.lane;
   const int h0 = kh * G;
-  float qf[G][NE];
-  uint32_t q2[G][NE / 2];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const size_t base = (static_cast<size_t>(b) * p.num_q_heads + h0 + g) * D + (j * LPT + lc) * EPL;
-      if constexpr (kDot2) {
-        const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + base);
-        q2[g][4 * j + 0] = x.x;
-        q2[g][4 * j + 1] = x.y;
-        q2[g][4 * j + 2] = x.z;
-        q2[g][4 * j + 3] = x.w;
-      } else if constexpr (QT == PKV_BF16) {
-        const uint16_t* qp = static_cast<const uint16_t*>(p.q) + base;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) qf[g][j * EPL + e] = __uint_as_float(static_cast<uint32_t>(qp[e]) << 16);
-      } else {
-        const float* qp = static_cast<const float*>(p.q) + base;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) qf[g][j * EPL + e] = qp[e];
-      }
-    }
-  }
+  wd.load_q(p.q, p.num_q_heads, b, h0);
 
   // Split 0 always starts at block 0, so its first table entries can be read
   // in the same round trip as q and the context length (entries past the
@@ -130,14 +84,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
   const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
   const int nb_w = nblk > w ? (nblk - w + NW - 1) / NW : 0;
 
-  float m[G], l[G], acc[G][NE];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = neg_inf();
-    l[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < NE; ++e) acc[g][e] = 0.f;
-  }
+  wd.reset();
 
   // ---- block ids: lane j of a 64-entry chunk holds the id of this wave's
   //      block (chunk*64 + j); ids outside the pool poison the result ----
@@ -168,166 +115,27 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
     id_chunk = 0;
     bad = bad || wave_any(lane_bad);
   }
+  auto tok0_of = [&](int it) { return t0 + (w + it * NW) * kBlock; };
 
-  struct Tile {
-    uint4 k[IPB][CPL];
-    uint4 v[IPB][CPL];
-    float ks[IPB];
-    float vs[IPB];
-  };
-
-  auto load_block = [&](int it, Tile& t) {
-    const int id = block_id(it);
-    const size_t tile = static_cast<size_t>(id) * p.num_kv_heads + kh;
-    // K/V are streamed once per call: non-temporal loads keep them from
-    // evicting the block tables, context lengths and q from the caches
-    const char* kt = static_cast<const char*>(p.k) + tile * kTileBytes;  // uniform base
-    const char* vt = static_cast<const char*>(p.v) + tile * kTileBytes;
+  // ---- stream the wave's blocks with PD blocks of K/V in flight ahead: a
+  //      ring of PD + 1 register tiles, indexed statically (fully unrolled) ----
+  Tile ring[PD + 1];
 #pragma unroll
-    for (int i = 0; i < IPB; ++i) {
+  for (int k = 0; k < PD; ++k)
+    if (k < nb_w) wd.load_tile(p, block_id(k), kh, ring[k]);
+  for (int it = 0; it < nb_w; it += PD + 1) {
 #pragma unroll
-      for (int j = 0; j < CPL; ++j)
-        t.k[i][j] = load_nt16(kt + lane_off + i * TPI * ROWB + j * LPT * 16);
+    for (int k = 0; k <= PD; ++k) {
+      const int cur = it + k;
+      if (cur + PD < nb_w) wd.load_tile(p, block_id(cur + PD), kh, ring[(k + PD) % (PD + 1)]);
+      if (cur < nb_w) wd.run(ring[k], tok0_of(cur), t1, p.scale_log2);
     }
-#pragma unroll
-    for (int i = 0; i < IPB; ++i) {
-#pragma unroll
-      for (int j = 0; j < CPL; ++j)
-        t.v[i][j] = load_nt16(vt + lane_off + i * TPI * ROWB + j * LPT * 16);
-    }
-    if constexpr (kI8) {
-#pragma unroll
-      for (int i = 0; i < IPB; ++i) {
-        t.ks[i] = p.k_scale[tile * kBlock + i * TPI + tslot];
-        t.vs[i] = p.v_scale[tile * kBlock + i * TPI + tslot];
-      }
-    }
-  };
-
-  auto process = [&](const Tile& t, int it, auto full_tag) {
-    constexpr bool kFull = decltype(full_tag)::value;
-    const int tok0 = t0 + (w + it * NW) * kBlock;
-    float sc[IPB][G];
-#pragma unroll
-    for (int i = 0; i < IPB; ++i) {
-      float kf[NE];
-      if constexpr (!kDot2) {
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) unpack16<KV>(t.k[i][j], kf + j * EPL);
-      }
-      const bool valid = kFull || (tok0 + i * TPI + tslot < t1);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float d = 0.f;
-        if constexpr (kDot2) {
-#pragma unroll
-          for (int j = 0; j < CPL; ++j) {
-            const uint32_t kw[4] = {t.k[i][j].x, t.k[i][j].y, t.k[i][j].z, t.k[i][j].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q2[g][4 * j + e]),
-                                                  __builtin_bit_cast(bf16x2_t, kw[e]), d, false);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < NE; ++e) d = fmaf(qf[g][e], kf[e], d);
-        }
-        d = group_sum<LPT>(d);
-        if constexpr (kI8) d *= t.ks[i] * p.scale_log2;
-        else d *= p.scale_log2;
-        if constexpr (!kFull) d = valid ? d : neg_inf();
-        sc[i][g] = d;
-      }
-    }
-    // online softmax: move the reference max only when a block exceeds it by
-    // more than the slack (or the slot had no finite score yet)
-    bool need = false;
-    float bm[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      bm[g] = sc[0][g];
-#pragma unroll
-      for (int i = 1; i < IPB; ++i) bm[g] = fmaxf(bm[g], sc[i][g]);
-      need = need || (bm[g] > m[g] + kRescaleSlack);
-    }
-    if (wave_any(need)) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        if (bm[g] > m[g] + kRescaleSlack) {
-          const float corr = __builtin_amdgcn_exp2f(m[g] - bm[g]);  // m = -inf -> 0
-          l[g] *= corr;
-#pragma unroll
-          for (int e = 0; e < NE; ++e) acc[g][e] *= corr;
-          m[g] = bm[g];
-        }
-      }
-    }
-    float pr[IPB][G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mu = (m[g] == neg_inf()) ? 0.f : m[g];
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < IPB; ++i) {
-        pr[i][g] = __builtin_amdgcn_exp2f(sc[i][g] - mu);  // -inf -> 0
-        sum += pr[i][g];
-      }
-      l[g] += sum;
-    }
-#pragma unroll
-    for (int i = 0; i < IPB; ++i) {
-      float vf[NE];
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) unpack16<KV>(t.v[i][j], vf + j * EPL);
-      // rows past the context (and their int8 scales) may hold NaN: masked
-      // tokens contribute by select, never as 0 * NaN
-      const bool valid = kFull || (tok0 + i * TPI + tslot < t1);
-      if constexpr (!kFull) {
-#pragma unroll
-        for (int e = 0; e < NE; ++e) vf[e] = valid ? vf[e] : 0.f;
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float pw = pr[i][g];
-        if constexpr (kI8) pw = (kFull || valid) ? pw * t.vs[i] : 0.f;
-#pragma unroll
-        for (int e = 0; e < NE; ++e) acc[g][e] = fmaf(pw, vf[e], acc[g][e]);
-      }
-    }
-  };
-
-  auto run = [&](const Tile& t, int it) {
-    const int tok0 = t0 + (w + it * NW) * kBlock;
-    if (tok0 + kBlock <= t1) process(t, it, std::true_type{});
-    else process(t, it, std::false_type{});
-  };
-
-  // ---- stream the wave's blocks, two blocks of K/V in flight ahead ----
-  Tile ta, tb, tc;
-  if (nb_w > 0) load_block(0, ta);
-  if (nb_w > 1) load_block(1, tb);
-  for (int it = 0; it < nb_w; it += 3) {
-    if (it + 2 < nb_w) load_block(it + 2, tc);
-    run(ta, it);
-    if (it + 3 < nb_w) load_block(it + 3, ta);
-    if (it + 1 < nb_w) run(tb, it + 1);
-    if (it + 4 < nb_w) load_block(it + 4, tb);
-    if (it + 2 < nb_w) run(tc, it + 2);
   }
 
   // ---- merge: bring the wave's token slots to one reference max ----
   float M[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float mm = m[g];
-#pragma unroll
-    for (int msk = LPT; msk < kWave; msk <<= 1) mm = fmaxf(mm, __shfl_xor(mm, msk));
-    M[g] = mm;
-    const float a = (m[g] == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(m[g] - mm);
-    l[g] *= a;
-#pragma unroll
-    for (int e = 0; e < NE; ++e) acc[g][e] *= a;
-  }
+  wd.slots_to_common_max(M);
+  const int tslot = wd.tslot, lc = wd.lc;
   if constexpr (kLdsMerge) {
     // every (wave, slot) state goes to LDS; the output threads sum them
 #pragma unroll
@@ -335,30 +143,22 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s_part[w][tslot][g][(j * LPT + lc) * EPL + e] = acc[g][j * EPL + e];
+        for (int e = 0; e < EPL; ++e) s_part[w][tslot][g][wd.dim_of(j, e)] = wd.acc[g][j * EPL + e];
       }
-      if (lc == 0) s_lp[w][tslot][g] = l[g];
+      if (lc == 0) s_lp[w][tslot][g] = wd.l[g];
     }
   } else {
     // sum the slots with lane shuffles first, then one state per wave
-#pragma unroll
-    for (int msk = LPT; msk < kWave; msk <<= 1) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        l[g] += __shfl_xor(l[g], msk);
-#pragma unroll
-        for (int e = 0; e < NE; ++e) acc[g][e] += __shfl_xor(acc[g][e], msk);
-      }
-    }
+    wd.sum_slots();
     if (lane < LPT) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) s_part[w][0][g][(j * LPT + lc) * EPL + e] = acc[g][j * EPL + e];
+          for (int e = 0; e < EPL; ++e) s_part[w][0][g][wd.dim_of(j, e)] = wd.acc[g][j * EPL + e];
         }
-        if (lc == 0) s_lp[w][0][g] = l[g];
+        if (lc == 0) s_lp[w][0][g] = wd.l[g];
       }
     }
   }
@@ -414,45 +214,358 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
   }
 }
 
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Number of 16-token blocks of a context length, 0 for lengths the table
+// cannot hold (those sequences are written by the empty-sequence pass).
+__device__ __forceinline__ int blocks_of(int n, int max_blocks) {
+  return (n > 0 && static_cast<int64_t>(n) <= static_cast<int64_t>(max_blocks) * kBlock) ? (n + kBlock - 1) / kBlock
+                                                                                        : 0;
+}
+
+// Balanced single-launch decode (see the file comment). Four wavefronts per
+// workgroup, each an independent worker; PD blocks of K/V in flight.
+template <int KV, int QT, int D, int G, int PD>
+__global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
+  using WD = WaveDecoder<KV, QT, D, G>;
+  using Tile = typename WD::Tile;
+  constexpr int LPT = WD::LPT, CPL = WD::CPL, EPL = WD::EPL;
+  constexpr int kPart = G * (D + 1);   // floats of one partial: o[G][D] then lse[G]
+
+  WD wd;
+  wd.init_lane();
+  const int lane = wd.lane;
+  const int nw_grid = gridDim.x * 4;
+  const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Hkv = p.num_kv_heads;
+  const int Hq = p.num_q_heads;
+
+  // ---- total tiles of the batch ----
+  int64_t T = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += kWave) {
+    const int bb = c0 + lane;
+    const int nb = bb < p.batch ? blocks_of(p.ctx[bb], p.max_blocks) : 0;
+    T += wave_sum_i32(nb);
+  }
+  T *= Hkv;
+
+  // ---- sequences without tiles: n == 0 -> (0, -inf); bad n -> NaN ----
+  for (int bb = gw; bb < p.batch; bb += nw_grid) {
+    const int n = p.ctx[bb];
+    if (blocks_of(n, p.max_blocks) > 0) continue;
+    const bool empty = (n == 0);
+    float* out = p.o + static_cast<size_t>(bb) * Hq * D;
+    for (int idx = lane; idx < Hq * D; idx += kWave) out[idx] = empty ? 0.f : qnan();
+    if (p.lse != nullptr)
+      for (int h = lane; h < Hq; h += kWave) p.lse[static_cast<size_t>(bb) * Hq + h] = empty ? neg_inf() : qnan();
+  }
+  if (T == 0) return;
+  // tiles are dealt over min(wavefronts, T) workers, so that every worker
+  // owns at least one tile and the workers that touch a segment are exactly
+  // the consecutive ones between its first and its last tile's owner
+  const int nw = static_cast<int>(T < nw_grid ? T : nw_grid);
+  if (gw >= nw) return;
+  const int64_t r0 = static_cast<int64_t>(gw) * T / nw;
+  const int64_t r1 = static_cast<int64_t>(gw + 1) * T / nw;
+  if (r0 >= r1) return;
+  auto wave_of = [&](int64_t t) -> int { return static_cast<int>(((t + 1) * nw - 1) / T); };
+
+  // ---- locate tile r0: sequence b, kv head kh, block blk ----
+  int b = 0;
+  int64_t base = 0;   // flat index of tile (b, kh = 0, blk = 0)
+  for (int c0 = 0; c0 < p.batch; c0 += kWave) {
+    const int bb = c0 + lane;
+    const int tiles = bb < p.batch ? Hkv * blocks_of(p.ctx[bb], p.max_blocks) : 0;
+    const int incl = wave_incl_scan_i32(tiles, lane);
+    const int total = __shfl(incl, kWave - 1);
+    if (base + total > r0) {
+      const uint64_t hit = __ballot(base + incl > r0);
+      const int first = __builtin_ctzll(hit);
+      b = c0 + first;
+      base += __shfl(incl, first) - __shfl(tiles, first);
+      break;
+    }
+    base += total;
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  int n = p.ctx[b];
+  int nb = blocks_of(n, p.max_blocks);
+  if (nb == 0) return;   // cannot happen for r0 < T; keeps the divisions below safe
+  int kh = static_cast<int>((r0 - base) / nb);
+  int blk = static_cast<int>((r0 - base) % nb);
+
+  // the load cursor runs PD tiles ahead of the processing cursor
+  int lb = b, lkh = kh, lblk = blk, lnb = nb;
+  int64_t lbase = base;
+  auto advance = [&](int& cb, int& ckh, int& cblk, int& cnb, int64_t& cbase) {
+    if (++cblk < cnb) return;
+    cblk = 0;
+    if (++ckh < Hkv) return;
+    ckh = 0;
+    cbase += static_cast<int64_t>(Hkv) * cnb;
+    do {
+      ++cb;
+      cnb = cb < p.batch ? blocks_of(p.ctx[cb], p.max_blocks) : 1;
+    } while (cnb == 0);
+  };
+
+  // block ids of the load cursor's sequence, 64 per fetch (lane j -> block c*64+j)
+  int id_b = -1, id_chunk = -1, ids = 0;
+  bool bad = false;   // an id outside the pool: the current segment comes out NaN
+  bool seg_bad = false;
+  auto block_id = [&](int cb, int cblk) -> int {
+    if (cb != id_b || (cblk >> 6) != id_chunk) {
+      id_b = cb;
+      id_chunk = cblk >> 6;
+      const int j = (id_chunk << 6) + lane;
+      int v = 0;
+      if (j < max(1, blocks_of(p.ctx[cb], p.max_blocks))) v = p.tables[static_cast<size_t>(cb) * p.max_blocks + j];
+      ids = v;
+    }
+    const int id = readlane(ids, cblk & 63);
+    return id;
+  };
+
+  Tile ring[PD + 1];
+  int ring_bad = 0;   // bit k: the id of ring[k] was outside the pool
+  int64_t lpos = r0;
+  auto issue = [&](int slot) {
+    const int id = block_id(lb, lblk);
+    const bool ok = static_cast<unsigned>(id) < static_cast<unsigned>(p.num_blocks);
+    ring_bad = ok ? (ring_bad & ~(1 << slot)) : (ring_bad | (1 << slot));
+    wd.load_tile(p, ok ? id : 0, lkh, ring[slot]);
+    advance(lb, lkh, lblk, lnb, lbase);
+    ++lpos;
+  };
+
+  wd.load_q(p.q, Hq, b, kh * G);
+  wd.reset();
+#pragma unroll
+  for (int k = 0; k < PD; ++k)
+    if (r0 + k < r1) issue(k);
+
+  auto finish_segment = [&](int sb, int skh, int snb, int64_t sbase, int sn) {
+    float M[G];
+    wd.slots_to_common_max(M);
+    wd.sum_slots();
+    const bool sbad = wave_any(seg_bad);
+    const int64_t seg_lo = sbase + static_cast<int64_t>(skh) * snb;
+    const int64_t seg_hi = seg_lo + snb;
+    const int h0 = skh * G;
+    if (seg_lo >= r0 && seg_hi <= r1) {
+      // the whole segment is this wavefront's: write the result
+      if (lane < LPT) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float L = wd.l[g];
+          const float inv = L > 0.f ? 1.f / L : 0.f;
+          float* out = p.o + (static_cast<size_t>(sb) * Hq + h0 + g) * D;
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) out[wd.dim_of(j, e)] = sbad ? qnan() : wd.acc[g][j * EPL + e] * inv;
+          }
+          if (lane == 0 && p.lse != nullptr)
+            p.lse[static_cast<size_t>(sb) * Hq + h0 + g] =
+                sbad ? qnan() : (L > 0.f ? (M[g] + log2f(L)) * kLn2 : neg_inf());
+        }
+      }
+    } else {
+      // A range boundary cuts the segment: leave a partial, the last one in
+      // merges. The XCDs' L2s are not coherent with each other, and a
+      // device-scope fence would write back / invalidate a whole L2; instead
+      // the partials are written and read with agent-coherent (sc1) accesses,
+      // and the counter is a device atomic, so only the exchanged bytes go
+      // to the coherent level.
+      const int slot = (seg_lo <= r0) ? 0 : 1;   // this wavefront's first segment, or its last
+      float* part = p.part + (static_cast<size_t>(gw) * 2 + slot) * kPart;
+      if (lane < LPT) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float L = wd.l[g];
+          const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+              __hip_atomic_store(part + g * D + wd.dim_of(j, e), sbad ? qnan() : wd.acc[g][j * EPL + e] * inv,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          if (lane == 0)
+            __hip_atomic_store(part + G * D + g, sbad ? qnan() : (L > 0.f ? (M[g] + log2f(L)) * kLn2 : neg_inf()),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the stores above have completed
+      int old = 0;
+      int32_t* cnt = p.counters + static_cast<size_t>(sb) * Hkv + skh;
+      if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old = __shfl(old, 0);
+      const int w_lo = wave_of(seg_lo);
+      const int w_hi = wave_of(seg_hi - 1);
+      if (old == w_hi - w_lo) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        // Merge the C contributors' partials, lane-parallel: every round of
+        // coherent loads is issued before any of it is used.
+        const int C = w_hi - w_lo + 1;
+        const int64_t start_lo = static_cast<int64_t>(w_lo) * T / nw;
+        auto part_of = [&](int c) -> const float* {
+          const int sl = (c == 0 && seg_lo > start_lo) ? 1 : 0;
+          return p.part + (static_cast<size_t>(w_lo + c) * 2 + sl) * kPart;
+        };
+        auto ld = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+        constexpr int kPerPass = kWave / G;                // contributors whose lse one pass loads
+        constexpr int kElems = G * D / kWave;              // output elements per lane: idx = lane + 64 k
+        constexpr int kChunk = 8;                          // contributors whose rows one round loads
+        const int mg = lane % G;
+        // 1. reference max of each head over the contributors
+        float mx = neg_inf();
+        bool nan = false;
+        for (int c0 = 0; c0 < C; c0 += kPerPass) {
+          const int c = c0 + lane / G;
+          const float x = c < C ? ld(part_of(c) + G * D + mg) : neg_inf();
+          nan = nan || (x != x);
+          mx = fmaxf(mx, x);
+        }
+#pragma unroll
+        for (int msk = G; msk < kWave; msk <<= 1) mx = fmaxf(mx, __shfl_xor(mx, msk));   // lane holds max of head lane % G
+        nan = wave_any(nan);
+        // 2. weights, denominators and weighted rows, kChunk contributors per round
+        float Lh = 0.f;                     // denominator of head lane % G (summed over lanes below)
+        float O[kElems];
+#pragma unroll
+        for (int k = 0; k < kElems; ++k) O[k] = 0.f;
+        for (int c0 = 0; c0 < C; c0 += kChunk) {
+          const int cw = c0 + lane / G;      // lanes 0 .. kChunk*G-1: contributor c0 + lane/G, head lane%G
+          float wt = 0.f;
+          if (lane < kChunk * G && cw < C && mx != neg_inf()) wt = __builtin_amdgcn_exp2f((ld(part_of(cw) + G * D + mg) - mx) * kLog2e);
+          Lh += wt;
+          float rows[kChunk][kElems];
+#pragma unroll
+          for (int cc = 0; cc < kChunk; ++cc) {
+#pragma unroll
+            for (int k = 0; k < kElems; ++k) rows[cc][k] = (c0 + cc < C) ? ld(part_of(c0 + cc) + lane + kWave * k) : 0.f;
+          }
+#pragma unroll
+          for (int cc = 0; cc < kChunk; ++cc) {
+#pragma unroll
+            for (int k = 0; k < kElems; ++k) {
+              const int gk = (lane + kWave * k) / D;
+              O[k] = fmaf(__shfl(wt, cc * G + gk), rows[cc][k], O[k]);
+            }
+          }
+        }
+        // denominators: lanes with the same lane % G hold parts of the same head's sum
+#pragma unroll
+        for (int msk = G; msk < kWave; msk <<= 1) Lh += __shfl_xor(Lh, msk);
+#pragma unroll
+        for (int k = 0; k < kElems; ++k) {
+          const int idx = lane + kWave * k;
+          const int gk = idx / D;
+          const float L = __shfl(Lh, gk);
+          const float M = __shfl(mx, gk);
+          const float o = nan ? qnan() : (L > 0.f ? O[k] / L : 0.f);
+          p.o[(static_cast<size_t>(sb) * Hq + h0) * D + idx] = o;
+          if (idx % D == 0 && p.lse != nullptr)
+            p.lse[static_cast<size_t>(sb) * Hq + h0 + gk] = nan ? qnan() : (L > 0.f ? M + logf(L) : neg_inf());
+        }
+        if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+      }
+    }
+    wd.reset();
+    seg_bad = false;
+    (void)sn;
+  };
+
+  int64_t pos = r0;
+  for (int64_t it = 0; pos < r1; it += PD + 1) {
+#pragma unroll
+    for (int k = 0; k <= PD; ++k) {
+      if (pos < r1) {
+        if (lpos < r1) issue((k + PD) % (PD + 1));
+        seg_bad = seg_bad || ((ring_bad >> k) & 1);
+        wd.run(ring[k], blk * kBlock, n, p.scale_log2);
+        ++pos;
+        // leaving the segment (or the range): finish it
+        const bool last_of_seg = (blk + 1 == nb);
+        if (last_of_seg || pos == r1) {
+          finish_segment(b, kh, nb, base, n);
+          if (pos < r1) {
+            advance(b, kh, blk, nb, base);
+            n = p.ctx[b];
+            wd.load_q(p.q, Hq, b, kh * G);
+          }
+        } else {
+          ++blk;
+        }
+      }
+    }
+  }
+}
+
 // Host-side dispatch over the compile-time shape parameters of one KV type.
-template <int KV, int QT, int D, int G, int NW>
+template <int KV, int QT, int D, int G, int NW, int PD>
 hipError_t launch_partial_t(const DecodeParams& p, hipStream_t st) {
   const int items = p.batch * (p.direct ? 1 : p.max_ns) * p.num_kv_heads;
   const int grid = (items + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((decode_partial_kernel<KV, QT, D, G, NW>), dim3(grid), dim3(NW * kWave), 0, st, p);
+  hipLaunchKernelGGL((decode_partial_kernel<KV, QT, D, G, NW, PD>), dim3(grid), dim3(NW * kWave), 0, st, p);
   return hipGetLastError();
 }
 
 template <int KV, int QT, int D, int G>
-hipError_t launch_partial_w(const DecodeParams& p, int waves, hipStream_t st) {
+hipError_t launch_balanced_t(const DecodeParams& p, int workgroups, hipStream_t st) {
+  hipLaunchKernelGGL((decode_balanced_kernel<KV, QT, D, G, 2>), dim3(workgroups), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+// waves: wavefronts per workgroup; deep: keep 5 blocks in flight per
+// wavefront instead of 2 (for grids that fit the chip in one pass, where
+// nothing else hides a wavefront's memory latency)
+template <int KV, int QT, int D, int G>
+hipError_t launch_partial_w(const DecodeParams& p, int waves, bool deep, hipStream_t st) {
+  if (waves < 0) return launch_balanced_t<KV, QT, D, G>(p, -waves, st);   // balanced: -workgroups
+  if (deep && waves == 4) return launch_partial_t<KV, QT, D, G, 4, 5>(p, st);
   switch (waves) {
-    case 2: return launch_partial_t<KV, QT, D, G, 2>(p, st);
-    case 4: return launch_partial_t<KV, QT, D, G, 4>(p, st);
-    case 8: return launch_partial_t<KV, QT, D, G, 8>(p, st);
+    case 2: return launch_partial_t<KV, QT, D, G, 2, 2>(p, st);
+    case 4: return launch_partial_t<KV, QT, D, G, 4, 2>(p, st);
+    case 8: return launch_partial_t<KV, QT, D, G, 8, 2>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int KV, int QT, int D>
-hipError_t launch_partial_g(const DecodeParams& p, int group, int waves, hipStream_t st) {
+hipError_t launch_partial_g(const DecodeParams& p, int group, int waves, bool deep, hipStream_t st) {
   switch (group) {
-    case 1: return launch_partial_w<KV, QT, D, 1>(p, waves, st);
-    case 2: return launch_partial_w<KV, QT, D, 2>(p, waves, st);
-    case 4: return launch_partial_w<KV, QT, D, 4>(p, waves, st);
-    case 8: return launch_partial_w<KV, QT, D, 8>(p, waves, st);
+    case 1: return launch_partial_w<KV, QT, D, 1>(p, waves, deep, st);
+    case 2: return launch_partial_w<KV, QT, D, 2>(p, waves, deep, st);
+    case 4: return launch_partial_w<KV, QT, D, 4>(p, waves, deep, st);
+    case 8: return launch_partial_w<KV, QT, D, 8>(p, waves, deep, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int KV>
-hipError_t launch_partial_kv(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves,
+hipError_t launch_partial_kv(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves, bool deep,
                              hipStream_t st) {
   if (q_dtype == PKV_F32) {
-    if (head_dim == 64) return launch_partial_g<KV, PKV_F32, 64>(p, group, waves, st);
-    if (head_dim == 128) return launch_partial_g<KV, PKV_F32, 128>(p, group, waves, st);
+    if (head_dim == 64) return launch_partial_g<KV, PKV_F32, 64>(p, group, waves, deep, st);
+    if (head_dim == 128) return launch_partial_g<KV, PKV_F32, 128>(p, group, waves, deep, st);
   } else if (q_dtype == PKV_BF16) {
-    if (head_dim == 64) return launch_partial_g<KV, PKV_BF16, 64>(p, group, waves, st);
-    if (head_dim == 128) return launch_partial_g<KV, PKV_BF16, 128>(p, group, waves, st);
+    if (head_dim == 64) return launch_partial_g<KV, PKV_BF16, 64>(p, group, waves, deep, st);
+    if (head_dim == 128) return launch_partial_g<KV, PKV_BF16, 128>(p, group, waves, deep, st);
   }
   return hipErrorInvalidValue;
 }

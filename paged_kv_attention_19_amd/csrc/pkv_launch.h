@@ -41,6 +41,8 @@ struct DecodeParams {
   int32_t max_ns;
   int32_t direct;          // 1: one split per sequence, normalised output to o/lse
   float scale_log2;        // softmax scale * log2(e)
+  float* part;             // balanced mode: partials of cut segments
+  int32_t* counters;       // balanced mode: one arrival counter per (sequence, kv head), zero between calls
 };
 
 struct CombineParams {
@@ -79,13 +81,15 @@ struct ChunkedParams {
 hipError_t launch_reshape(const ReshapeParams& p, int src_dtype, int kv_dtype, int head_dim,
                           hipStream_t stream);
 // Decode partial pass, one entry per KV element type; `waves` (2, 4, 8)
-// is the number of wavefronts per workgroup.
+// is the number of wavefronts per workgroup, `deep` asks for 5 blocks in
+// flight per wavefront (built with 4 wavefronts). A negative `waves` launches
+// the balanced single-pass decode on -waves workgroups instead.
 hipError_t launch_decode_partial_f32(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves,
-                                     hipStream_t stream);
+                                     bool deep, hipStream_t stream);
 hipError_t launch_decode_partial_bf16(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves,
-                                      hipStream_t stream);
+                                      bool deep, hipStream_t stream);
 hipError_t launch_decode_partial_i8(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves,
-                                    hipStream_t stream);
+                                    bool deep, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_chunked(const ChunkedParams& p, int kv_dtype, int head_dim, int group,
                           hipStream_t stream);
