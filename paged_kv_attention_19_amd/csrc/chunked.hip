@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   __shared__ __attribute__((aligned(16))) float s_ks[2][kTile];
   __shared__ __attribute__((aligned(16))) float s_vs[2][kTile];
   constexpr int kIdsCached = 1024;          // block ids kept in LDS (16384 tokens)
-  __shared__ int s_ids[kIdsCached];
+  __shared__ __attribute__((aligned(16))) int s_ids[kIdsCached];
 
   // ---- work item: (sequence, kv head, query tile), XCD-contiguous ----
   const int QT = (p.max_q_len + P - 1) / P;
@@ -153,32 +153,44 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   for (int j = tid; j < min(nblk_need, kIdsCached); j += kThreads) s_ids[j] = trow[j];
   __syncthreads();
 
-  auto block_of = [&](int tile, int bi, int& id) -> bool {
-    const int blk = tile * (kTile / kBlock) + bi;
-    if (blk >= nblk_seq) return false;
-    id = blk < kIdsCached ? s_ids[blk] : trow[blk];
-    if (static_cast<unsigned>(id) >= static_cast<unsigned>(p.num_blocks)) {
-      bad = 1;
-      return false;
+  // Block ids of the 4 blocks of a tile (uniform), read before any of the
+  // tile's loads are issued: a lookup between them would make every later
+  // load wait for the earlier ones. ok bit bi: block bi exists and is valid.
+  auto tile_ids = [&](int tile, int (&id)[4]) -> unsigned {
+    const int blk0 = tile * (kTile / kBlock);
+    if (blk0 + 4 <= kIdsCached) {
+      const int4 x = *reinterpret_cast<const int4*>(&s_ids[blk0]);
+      id[0] = x.x; id[1] = x.y; id[2] = x.z; id[3] = x.w;
+    } else {
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) id[bi] = blk0 + bi < nblk_seq ? trow[blk0 + bi] : 0;
     }
-    return true;
+    unsigned ok = 0;
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      id[bi] = __builtin_amdgcn_readfirstlane(id[bi]);
+      if (blk0 + bi < nblk_seq) {
+        if (static_cast<unsigned>(id[bi]) < static_cast<unsigned>(p.num_blocks)) ok |= 1u << bi;
+        else bad = 1;
+      }
+    }
+    return ok;
   };
 
   auto gload = [&](int tile) {
     const int u = tid & 15;
     const int t0 = tile * kTile;
     constexpr int kRowBytes = kI8 ? kD : 2 * kD;
+    int id[4];
+    const unsigned ok = tile_ids(tile, id);
     // K chunk i sits in block i of the tile; V chunks of this wavefront in block w
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int id = 0;
       const int tok = t0 + 16 * i + (tid >> 4);
       stk[i] = make_uint4(0, 0, 0, 0);
-      const bool ok = block_of(tile, i, id);
-      id = __builtin_amdgcn_readfirstlane(id);
-      if (ok && tok < n) {
+      if (((ok >> i) & 1u) && tok < n) {
         const char* base = static_cast<const char*>(p.k) +
-                           (static_cast<size_t>(id) * p.num_kv_heads + kh) * kBlock * kRowBytes;
+                           (static_cast<size_t>(id[i]) * p.num_kv_heads + kh) * kBlock * kRowBytes;
         const int off = (tid >> 4) * kRowBytes + u * (kRowBytes / 16);
         if constexpr (kI8) {
           const uint2 c = *reinterpret_cast<const uint2*>(base + off);
@@ -190,16 +202,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     }
     const int tg = tid >> 4;
     {
-      int id = 0;
-      const bool ok = block_of(tile, w, id);   // tokens 4 tg .. 4 tg + 3 lie in block tg / 4 == w
-      id = __builtin_amdgcn_readfirstlane(id);
+      // tokens 4 tg .. 4 tg + 3 lie in block tg / 4 == w
+      const int wu = __builtin_amdgcn_readfirstlane(w);
+      const int idw = wu == 0 ? id[0] : wu == 1 ? id[1] : wu == 2 ? id[2] : id[3];
+      const bool okw = (ok >> wu) & 1u;
       const char* base = static_cast<const char*>(p.v) +
-                         (static_cast<size_t>(id) * p.num_kv_heads + kh) * kBlock * kRowBytes;
+                         (static_cast<size_t>(idw) * p.num_kv_heads + kh) * kBlock * kRowBytes;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = t0 + 4 * tg + i;
         stv[i] = make_uint4(0, 0, 0, 0);
-        if (ok && tok < n) {
+        if (okw && tok < n) {
           const int off = (4 * (tg & 3) + i) * kRowBytes + u * (kRowBytes / 16);
           if constexpr (kI8) {
             const uint2 c = *reinterpret_cast<const uint2*>(base + off);
@@ -211,16 +224,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       }
     }
     if constexpr (kI8) {
-      // one scale per token: threads 0..63 fetch the tile's K scales (pre-multiplied
-      // by the softmax scale), 64..127 the V scales
+      // one scale per token: threads 0..63 fetch the tile's K scales, 64..127
+      // the V scales
       sks = 0.f;
       if (tid < 2 * kTile) {
         const int tt = tid & (kTile - 1);
         const int tok = t0 + tt;
-        int id = 0;
-        if (block_of(tile, tt >> 4, id) && tok < n) {
-          const size_t srow = (static_cast<size_t>(id) * p.num_kv_heads + kh) * kBlock + (tt & 15);
-          sks = tid < kTile ? p.k_scale[srow] * p.scale_log2 : p.v_scale[srow];
+        const int bi = tt >> 4;
+        const int ids = bi == 0 ? id[0] : bi == 1 ? id[1] : bi == 2 ? id[2] : id[3];
+        if (((ok >> bi) & 1u) && tok < n) {
+          const size_t srow = (static_cast<size_t>(ids) * p.num_kv_heads + kh) * kBlock + (tt & 15);
+          // raw scale: any arithmetic on it here would wait for all the tile's loads
+          sks = (tid < kTile ? p.k_scale : p.v_scale)[srow];
         }
       }
     }
@@ -266,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       *reinterpret_cast<uint2*>(vb + vt_addr(d, tg >> 1) + ((tg & 1) << 3)) = make_uint2(lo, hi);
     }
     if constexpr (kI8) {
-      if (tid < kTile) s_ks[buf][tid] = sks;
+      if (tid < kTile) s_ks[buf][tid] = sks * p.scale_log2;   // K scale x softmax scale
       else if (tid < 2 * kTile) s_vs[buf][tid - kTile] = sks;
     }
   };
