@@ -124,6 +124,21 @@ def copy_calibration(nbytes: int) -> None:
     print(json.dumps({"copy_bytes": nbytes, "copies": 8}), flush=True)
 
 
+def copy_reference(nbytes: int):
+    """A plain device-to-device copy that moves the same number of HBM bytes as
+    one decode launch (nbytes / 2 read, nbytes / 2 written), rotated over
+    enough buffers that every copy comes from HBM: the rate a memory-bound
+    kernel of this size can reach on this machine with no attention work."""
+    import torch
+    copies, steps = (16, 2048) if nbytes < (64 << 20) else (2, 64)
+    half = max(16, (nbytes // 2) // 16 * 16)
+    pairs = [(torch.randint(0, 255, (half,), dtype=torch.uint8, device="cuda:0"),
+              torch.empty(half, dtype=torch.uint8, device="cuda:0")) for _ in range(copies)]
+    sec = time_graphs(lambda pr: pr[1].copy_(pr[0]), pairs, steps, 256, 64)
+    us = sec / steps * 1e6
+    return {"bytes_moved": 2 * half, "us": round(us, 3), "GB/s": round(2 * half / (sec / steps) / 1e9, 1)}
+
+
 class Replica:
     """One independent copy of the workload, resident on the GPU."""
 
@@ -463,6 +478,7 @@ def main():
             "traffic": traffic,
         },
     }
+    line["copy_reference"] = copy_reference(int(partial_bytes))
     if not args.no_chunked:
         log("timing the chunked prefill ...")
         line["chunked_prefill"] = measure_chunked(dev)
