@@ -25,11 +25,23 @@
 // K rows are fed to the first product in an order that swaps bits 2 and 3 of
 // the row index; with it, the token order of the S^T registers is exactly the
 // k order the second product needs, so P never moves between lanes.
-// K is staged row-major and V transposed in LDS (the token index must be the
-// MFMA k dimension), both XOR-swizzled against bank conflicts, double
-// buffered: the next tile's global loads are in flight while this tile's
-// MFMAs run. An int8 cache is dequantized on its way to LDS (codes are exact in
-// bf16): the K scale multiplies the score column, the V scale the weight.
+//
+// Pipeline. K is staged row-major and V transposed (the token index must be
+// the MFMA k dimension) in a ring of three LDS stages, XOR-swizzled against
+// bank conflicts. Iteration j runs two independent pairs of work, each in one
+// straight-line block, so that the wavefront's VALU work issues while its
+// MFMAs execute:
+//   1. the softmax of tile j's scores  ||  S^T of tile j + 1 (MFMA);
+//   2. O^T += V_j^T P_j^T (MFMA)       ||  tile j + 2: registers -> LDS.
+// Global loads run two iterations ahead, into two register sets, as buffer
+// loads whose range is the valid part of each block: rows past the context
+// and blocks outside the table come back as zeros with no branch, so every
+// tile issues the same loads and only the older set is waited for. An int8
+// cache is dequantized on its way to LDS (codes are exact in bf16): the K
+// scale multiplies the score column, the V scale the weight.
+#include <type_traits>
+#include <utility>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -39,20 +51,29 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;            // head_dim built
 constexpr int kRows = 128;         // query rows per workgroup
 constexpr int kTile = 64;          // tokens per KV tile
 constexpr int kThreads = 256;
 constexpr int kXcdsC = 8;
-
-// LDS byte offsets
+constexpr int kStages = 3;
 constexpr int kKBytes = kTile * kD * 2;    // 16 KiB, row-major [token][dim], swizzled
 constexpr int kVBytes = kD * kTile * 2;    // 16 KiB, transposed [dim][token], swizzled
+constexpr int kStageBytes = kKBytes + kVBytes;
+constexpr int kIdsCached = 4096;           // block ids kept in LDS (65536 tokens)
+constexpr int kRsrcWord3 = 0x00020000;     // buffer descriptor word 3 (gfx9 family): raw dwords
 
-__device__ __forceinline__ int k_addr(int t, int unit) { return t * 256 + ((unit ^ (t & 15)) << 4); }
-__device__ __forceinline__ int vt_sw(int d) { return ((d >> 1) ^ (d >> 3)) & 7; }
-__device__ __forceinline__ int vt_addr(int d, int unit) { return d * 128 + ((unit ^ vt_sw(d)) << 4); }
+// Row order of the S^T product: bits 2 and 3 of the row index swapped.
+__device__ __forceinline__ int sigma(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+// K row t, 16-byte unit u (8 dims). The XOR key sigma(t) makes the 16 lanes
+// of one operand read (rows sigma(0..15), one unit) hit 16 different units.
+__device__ __forceinline__ int k_off(int t, int u) { return t * 256 + ((u ^ (sigma(t) & 15)) << 4); }
+// V^T row d (one dim: 64 tokens = 8 units of 8 tokens).
+__device__ __forceinline__ int vt_sw(int d) { return (d ^ (d >> 3) ^ (d >> 6)) & 7; }
+__device__ __forceinline__ int vt_off(int d, int u) { return d * 128 + ((u ^ vt_sw(d)) << 4); }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
@@ -65,15 +86,29 @@ __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int byte0) {
   return pack_bf16(a, b);
 }
 
+// Raw buffer over `bytes` bytes at `base`: loads at or past `bytes` return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 lds_read16(const char* a) { return *reinterpret_cast<const uint4*>(a); }
+
+// One tile's global loads, held in registers until they are stored to LDS.
+struct Staged {
+  uint4 k[4];      // K chunk i: block i, row thread / 16, 16-byte unit thread % 16
+  uint4 v[4];      // V chunk i: block w, row 4 (tg % 4) + i, same unit
+  float sc;        // int8: one K (thread % 128 < 64) or V scale of the tile
+  bool sc_ok;      // that token exists
+};
+
 template <int KV, int G>
 __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   constexpr int P = kRows / G;               // positions per query tile
   constexpr bool kI8 = (KV == PKV_I8);
   constexpr float kSlack = 8.0f;
-  __shared__ __attribute__((aligned(16))) char s_kv[2][kKBytes + kVBytes];
-  __shared__ __attribute__((aligned(16))) float s_ks[2][kTile];
-  __shared__ __attribute__((aligned(16))) float s_vs[2][kTile];
-  constexpr int kIdsCached = 1024;          // block ids kept in LDS (16384 tokens)
+  constexpr int kRowBytes = kI8 ? kD : 2 * kD;   // bytes of one cached K or V row
+  __shared__ __attribute__((aligned(16))) char s_kv[kStages][kStageBytes];
+  __shared__ __attribute__((aligned(16))) float s_sc[kStages][2 * kTile];   // int8: K scale x softmax scale, V scale
   __shared__ __attribute__((aligned(16))) int s_ids[kIdsCached];
 
   // ---- work item: (sequence, kv head, query tile), XCD-contiguous ----
@@ -137,25 +172,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   const int ntiles = (kv_end + kTile - 1) / kTile;
   const int first_diag = (n - L + qt * P) / kTile;   // tiles >= this one need the causal mask
   const int nblk_seq = (n + kBlock - 1) / kBlock;
+  const int nblk_need = min(nblk_seq, ntiles * (kTile / kBlock));   // the blocks of tiles < ntiles
   const int32_t* trow = p.tables + static_cast<size_t>(seq) * p.max_blocks;
-
-  // staging registers for one tile: K 4 chunks, V 4 chunks per thread
-  uint4 stk[4];
-  uint4 stv[4];
-  float sks = 0.f;
   int bad = 0;
 
-  // K chunk i: token 16 i + tid / 16, unit tid % 16 (8 dims)
-  // V chunk i: token 4 (tid / 16) + i, unit tid % 16
   // the block ids this tile range needs, read once into LDS (ids past what
   // LDS holds are read from the table when used)
-  const int nblk_need = min(nblk_seq, ntiles * (kTile / kBlock));
   for (int j = tid; j < min(nblk_need, kIdsCached); j += kThreads) s_ids[j] = trow[j];
   __syncthreads();
 
   // Block ids of the 4 blocks of a tile (uniform), read before any of the
-  // tile's loads are issued: a lookup between them would make every later
-  // load wait for the earlier ones. ok bit bi: block bi exists and is valid.
+  // tile's loads are issued. ok bit bi: block bi is one this tile range needs
+  // and its id is inside the pool; a needed id outside the pool poisons the
+  // output instead.
   auto tile_ids = [&](int tile, int (&id)[4]) -> unsigned {
     const int blk0 = tile * (kTile / kBlock);
     if (blk0 + 4 <= kIdsCached) {
@@ -163,13 +192,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       id[0] = x.x; id[1] = x.y; id[2] = x.z; id[3] = x.w;
     } else {
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi) id[bi] = blk0 + bi < nblk_seq ? trow[blk0 + bi] : 0;
+      for (int bi = 0; bi < 4; ++bi) id[bi] = blk0 + bi < nblk_need ? trow[blk0 + bi] : 0;
     }
     unsigned ok = 0;
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
       id[bi] = __builtin_amdgcn_readfirstlane(id[bi]);
-      if (blk0 + bi < nblk_seq) {
+      if (blk0 + bi < nblk_need) {
         if (static_cast<unsigned>(id[bi]) < static_cast<unsigned>(p.num_blocks)) ok |= 1u << bi;
         else bad = 1;
       }
@@ -177,112 +206,162 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     return ok;
   };
 
-  auto gload = [&](int tile) {
-    const int u = tid & 15;
-    const int t0 = tile * kTile;
-    constexpr int kRowBytes = kI8 ? kD : 2 * kD;
+  const int u16 = tid & 15;
+  const int tg = tid >> 4;
+  const char* kpool = static_cast<const char*>(p.k);
+  const char* vpool = static_cast<const char*>(p.v);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+
+  // Where tile `tile`'s loads come from: buffer descriptors over the valid
+  // rows of its blocks (none for blocks the range does not need), and this
+  // thread's scale. Any tile index is safe.
+  struct TileSrc {
+    __amdgpu_buffer_rsrc_t k[4];   // block i of the tile
+    __amdgpu_buffer_rsrc_t v;      // block w: this wavefront's V rows
+    const float* sc;               // int8: K scale (thread % 128 < 64) or V scale of token thread % 64
+    bool sc_ok;
+  };
+  const float* sc_pool = (tid & kTile) ? p.v_scale : p.k_scale;
+  auto tile_src = [&](int tile, TileSrc& ts) {
     int id[4];
     const unsigned ok = tile_ids(tile, id);
-    // K chunk i sits in block i of the tile; V chunks of this wavefront in block w
+    const int blk0 = tile * (kTile / kBlock);
+    int rows[4];
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      rows[bi] = ((ok >> bi) & 1u) ? min(kBlock, n - (blk0 + bi) * kBlock) : 0;   // valid rows of block bi
+      id[bi] = ((ok >> bi) & 1u) ? id[bi] : 0;
+      ts.k[bi] = rsrc(kpool + (static_cast<size_t>(id[bi]) * p.num_kv_heads + kh) * kBlock * kRowBytes,
+                      rows[bi] * kRowBytes);
+    }
+    int idw = id[0], roww = rows[0];
+#pragma unroll
+    for (int bi = 1; bi < 4; ++bi) {
+      idw = wu == bi ? id[bi] : idw;
+      roww = wu == bi ? rows[bi] : roww;
+    }
+    ts.v = rsrc(vpool + (static_cast<size_t>(idw) * p.num_kv_heads + kh) * kBlock * kRowBytes, roww * kRowBytes);
+    if constexpr (kI8) {
+      const int tt = tid & (kTile - 1);
+      const int bs = tt >> 4;
+      int ids = id[0], rws = rows[0];
+#pragma unroll
+      for (int bi = 1; bi < 4; ++bi) {
+        ids = bs == bi ? id[bi] : ids;
+        rws = bs == bi ? rows[bi] : rws;
+      }
+      ts.sc_ok = (tt & 15) < rws;
+      ts.sc = sc_pool + (static_cast<size_t>(ids) * p.num_kv_heads + kh) * kBlock + (tt & 15);
+    }
+  };
+  // The loads themselves: the same 8 (+1 scale) loads for every tile, no branch.
+  const int koff = tg * kRowBytes + u16 * (kRowBytes / 16);             // K chunk i: row tg of block i
+  const int voff = 4 * (tg & 3) * kRowBytes + u16 * (kRowBytes / 16);   // V chunk i: row 4 (tg % 4) + i of block w
+  auto gissue = [&](const TileSrc& ts, Staged& st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = t0 + 16 * i + (tid >> 4);
-      stk[i] = make_uint4(0, 0, 0, 0);
-      if (((ok >> i) & 1u) && tok < n) {
-        const char* base = static_cast<const char*>(p.k) +
-                           (static_cast<size_t>(id[i]) * p.num_kv_heads + kh) * kBlock * kRowBytes;
-        const int off = (tid >> 4) * kRowBytes + u * (kRowBytes / 16);
-        if constexpr (kI8) {
-          const uint2 c = *reinterpret_cast<const uint2*>(base + off);
-          stk[i] = make_uint4(c.x, c.y, 0, 0);
-        } else {
-          stk[i] = *reinterpret_cast<const uint4*>(base + off);
-        }
+      if constexpr (kI8) {
+        const u32x2v_t c = __builtin_bit_cast(u32x2v_t, __builtin_amdgcn_raw_buffer_load_b64(ts.k[i], koff, 0, 0));
+        st.k[i] = make_uint4(c.x, c.y, 0, 0);
+      } else {
+        const u32x4v_t c = __builtin_bit_cast(u32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(ts.k[i], koff, 0, 0));
+        st.k[i] = make_uint4(c.x, c.y, c.z, c.w);
       }
     }
-    const int tg = tid >> 4;
-    {
-      // tokens 4 tg .. 4 tg + 3 lie in block tg / 4 == w
-      const int wu = __builtin_amdgcn_readfirstlane(w);
-      const int idw = wu == 0 ? id[0] : wu == 1 ? id[1] : wu == 2 ? id[2] : id[3];
-      const bool okw = (ok >> wu) & 1u;
-      const char* base = static_cast<const char*>(p.v) +
-                         (static_cast<size_t>(idw) * p.num_kv_heads + kh) * kBlock * kRowBytes;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + 4 * tg + i;
-        stv[i] = make_uint4(0, 0, 0, 0);
-        if (okw && tok < n) {
-          const int off = (4 * (tg & 3) + i) * kRowBytes + u * (kRowBytes / 16);
-          if constexpr (kI8) {
-            const uint2 c = *reinterpret_cast<const uint2*>(base + off);
-            stv[i] = make_uint4(c.x, c.y, 0, 0);
-          } else {
-            stv[i] = *reinterpret_cast<const uint4*>(base + off);
-          }
-        }
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (kI8) {
+        const u32x2v_t c = __builtin_bit_cast(
+            u32x2v_t, __builtin_amdgcn_raw_buffer_load_b64(ts.v, voff + i * kRowBytes, 0, 0));
+        st.v[i] = make_uint4(c.x, c.y, 0, 0);
+      } else {
+        const u32x4v_t c = __builtin_bit_cast(
+            u32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(ts.v, voff + i * kRowBytes, 0, 0));
+        st.v[i] = make_uint4(c.x, c.y, c.z, c.w);
       }
     }
     if constexpr (kI8) {
-      // one scale per token: threads 0..63 fetch the tile's K scales, 64..127
-      // the V scales
-      sks = 0.f;
-      if (tid < 2 * kTile) {
-        const int tt = tid & (kTile - 1);
-        const int tok = t0 + tt;
-        const int bi = tt >> 4;
-        const int ids = bi == 0 ? id[0] : bi == 1 ? id[1] : bi == 2 ? id[2] : id[3];
-        if (((ok >> bi) & 1u) && tok < n) {
-          const size_t srow = (static_cast<size_t>(ids) * p.num_kv_heads + kh) * kBlock + (tt & 15);
-          // raw scale: any arithmetic on it here would wait for all the tile's loads
-          sks = (tid < kTile ? p.k_scale : p.v_scale)[srow];
-        }
-      }
+      st.sc = *ts.sc;
+      st.sc_ok = ts.sc_ok;
     }
   };
+  auto gload = [&](int tile, Staged& st) {
+    TileSrc ts;
+    tile_src(tile, ts);
+    gissue(ts, st);
+  };
 
-  auto lstore = [&](int buf) {
-    char* kb = s_kv[buf];
-    char* vb = s_kv[buf] + kKBytes;
-    const int u = tid & 15;
+  // LDS byte offsets of this thread's stores, the same for every stage
+  const int kw_off = k_off(tg, u16);                // K chunk i: token 16 i + tg, + 4096 i
+  int vw_off[8];                                    // V^T dim 8 u + e, tokens 4 tg .. +3
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vw_off[e] = kKBytes + vt_off(8 * u16 + e, tg >> 1) + ((tg & 1) << 3);
+
+  auto lstore = [&](const Staged& st, int stage) {
+    char* sb = s_kv[stage];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint4 x = stk[i];
+      uint4 x = st.k[i];
       if constexpr (kI8) {
-        x = make_uint4(i8pair_to_bf16x2(stk[i].x, 0), i8pair_to_bf16x2(stk[i].x, 2), i8pair_to_bf16x2(stk[i].y, 0),
-                       i8pair_to_bf16x2(stk[i].y, 2));
+        x = make_uint4(i8pair_to_bf16x2(st.k[i].x, 0), i8pair_to_bf16x2(st.k[i].x, 2),
+                       i8pair_to_bf16x2(st.k[i].y, 0), i8pair_to_bf16x2(st.k[i].y, 2));
       }
-      *reinterpret_cast<uint4*>(kb + k_addr(16 * i + (tid >> 4), u)) = x;
+      *reinterpret_cast<uint4*>(sb + kw_off + 4096 * i) = x;
     }
     // transpose V: thread holds tokens 4 tg .. 4 tg + 3 of dims 8 u .. 8 u + 7
     uint32_t vw[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (kI8) {
-        vw[i][0] = i8pair_to_bf16x2(stv[i].x, 0);
-        vw[i][1] = i8pair_to_bf16x2(stv[i].x, 2);
-        vw[i][2] = i8pair_to_bf16x2(stv[i].y, 0);
-        vw[i][3] = i8pair_to_bf16x2(stv[i].y, 2);
+        vw[i][0] = i8pair_to_bf16x2(st.v[i].x, 0);
+        vw[i][1] = i8pair_to_bf16x2(st.v[i].x, 2);
+        vw[i][2] = i8pair_to_bf16x2(st.v[i].y, 0);
+        vw[i][3] = i8pair_to_bf16x2(st.v[i].y, 2);
       } else {
-        vw[i][0] = stv[i].x;
-        vw[i][1] = stv[i].y;
-        vw[i][2] = stv[i].z;
-        vw[i][3] = stv[i].w;
+        vw[i][0] = st.v[i].x;
+        vw[i][1] = st.v[i].y;
+        vw[i][2] = st.v[i].z;
+        vw[i][3] = st.v[i].w;
       }
     }
-    const int tg = tid >> 4;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       // dim 8 u + e of the 4 tokens: low or high half of word e / 2 of each token
       const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
       const uint32_t lo = __builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel);
       const uint32_t hi = __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel);
-      const int d = 8 * u + e;
-      *reinterpret_cast<uint2*>(vb + vt_addr(d, tg >> 1) + ((tg & 1) << 3)) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(sb + vw_off[e]) = make_uint2(lo, hi);
     }
     if constexpr (kI8) {
-      if (tid < kTile) s_ks[buf][tid] = sks * p.scale_log2;   // K scale x softmax scale
-      else if (tid < 2 * kTile) s_vs[buf][tid - kTile] = sks;
+      // threads t and t + 128 store the same value to the same place
+      const float sc = st.sc_ok ? st.sc : 0.f;
+      s_sc[stage][tid & (2 * kTile - 1)] = (tid & kTile) ? sc : sc * p.scale_log2;
+    }
+  };
+
+  // LDS byte offsets of this lane's MFMA operand reads, the same for every stage
+  const int ar = lane & 31;
+  int kr_off[8];                                    // K row sigma(ar) (+ 32 rows: + 8192), unit 2 ks + h
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) kr_off[ks] = k_off(sigma(ar), 2 * ks + h);
+  int vr_off[4][4];                                 // V^T row 32 db + ar, unit 2 ks + h
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) vr_off[db][ks] = kKBytes + vt_off(32 * db + ar, 2 * ks + h);
+  }
+
+  // S^T of the tile in `stage`, for its two 32-token halves
+  auto qk = [&](int stage, f32x16_t (&s)[2]) {
+    const char* kb = s_kv[stage];
+    s[0] = f32x16_t{};
+    s[1] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 a0 = lds_read16(kb + kr_off[ks]);
+      const uint4 a1 = lds_read16(kb + kr_off[ks] + 8192);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), qb[ks], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), qb[ks], s[1], 0, 0, 0);
     }
   };
 
@@ -291,118 +370,233 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
+  f32x16_t sacc[2];   // S^T of the tile being softmaxed
 
-  // row r of an S^T block is K token sigma(r): bits 2 and 3 of r swapped
-  const int ar = lane & 31;
-  const int a_tok = (ar & 3) | ((ar & 4) << 1) | ((ar & 8) >> 1) | (ar & 16);
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < ntiles) gload(it + 1);
-    const char* kb = s_kv[buf];
-    const char* vb = s_kv[buf] + kKBytes;
-
-    // S^T for the two 32-token halves of the tile
-    f32x16_t sacc[2];
+  // Iteration j: phase 1 = softmax of tile j || S^T of tile j + 1; phase 2 =
+  // O^T += V_j^T P_j^T || tile j + 2 from registers to LDS, tile j + 4's
+  // loads. Each phase is written as slots of two MFMAs plus a share of the
+  // VALU / LDS work, fenced so the compiler keeps the interleaving; operand
+  // reads run ahead of their MFMAs, and MFMAs on the same accumulator are
+  // never adjacent.
+  auto phase1 = [&](auto diag_tag, int j, int sk, int ss, f32x16_t (&sn)[2], bf16x8_t (&phi)[4],
+                    bf16x8_t (&plo)[4], uint4 (&va0)[4], int sv_stage) -> float {
+    constexpr bool kDiag = decltype(diag_tag)::value;
+    const char* kb = s_kv[sk];            // K of tile j + 1
+    const float* scs = s_sc[ss];          // int8 scales of tile j
+    const int tlim = pos - j * kTile;     // tile tokens past this one are masked
+    uint4 ka[3][2];
+    auto read_k = [&](int ks, uint4 (&dst)[2]) {
+      dst[0] = lds_read16(kb + kr_off[ks]);
+      dst[1] = lds_read16(kb + kr_off[ks] + 8192);
+    };
+    // scores of chunk c = (half nb = c / 2, registers 8 (c % 2) .. + 7):
+    // tokens 32 nb + 8 h + 16 (c % 2) + e, e = 0 .. 7
+    auto sc_off = [&](int c) { return 32 * (c >> 1) + 8 * h + 16 * (c & 1); };
+    float4 sc4[2];
+    auto read_sc = [&](int off) {
+      sc4[0] = *reinterpret_cast<const float4*>(scs + off);
+      sc4[1] = *reinterpret_cast<const float4*>(scs + off + 4);
+    };
+    read_k(0, ka[0]);
+    read_k(1, ka[1]);
+    read_k(2, ka[2]);
+    if constexpr (kI8) read_sc(sc_off(0));
+    float sv[4][8];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      sacc[nb] = f32x16_t{};
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(kb + k_addr(32 * nb + a_tok, 2 * ks + h));
-        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qb[ks], sacc[nb], 0, 0, 0);
-      }
+      for (int e = 0; e < 8; ++e) sv[c][e] = sacc[c >> 1][8 * (c & 1) + e];
     }
-
-    // int8: the scales of this lane's 32 tokens, as runs of 8 (float4 reads)
-    float ksv[2][16], vsv[2][16];
-    if constexpr (kI8) {
+    sn[0] = f32x16_t{};
+    sn[1] = f32x16_t{};
+    auto mfma2 = [&](int ks) {
+      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks % 3][0]), qb[ks], sn[0], 0, 0, 0);
+      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks % 3][1]), qb[ks], sn[1], 0, 0, 0);
+      if (ks + 3 < 8) read_k(ks + 3, ka[ks % 3]);
+    };
+    // slots 0-3: scale, mask and max of chunk c
+    float cmax = neg_inf();
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+    for (int c = 0; c < 4; ++c) {
+      mfma2(c);
+      float kv[8];
+      if constexpr (kI8) {
+        kv[0] = sc4[0].x; kv[1] = sc4[0].y; kv[2] = sc4[0].z; kv[3] = sc4[0].w;
+        kv[4] = sc4[1].x; kv[5] = sc4[1].y; kv[6] = sc4[1].z; kv[7] = sc4[1].w;
+        read_sc(c < 3 ? sc_off(c + 1) : kTile + sc_off(0));   // next: K scales of chunk c + 1, then V of chunk 0
+      }
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int t0 = 32 * nb + 8 * h + 16 * half;
-#pragma unroll
-          for (int q4 = 0; q4 < 2; ++q4) {
-            const float4 a = *reinterpret_cast<const float4*>(&s_ks[buf][t0 + 4 * q4]);
-            const float4 b = *reinterpret_cast<const float4*>(&s_vs[buf][t0 + 4 * q4]);
-            const int v0 = 8 * half + 4 * q4;
-            ksv[nb][v0] = a.x; ksv[nb][v0 + 1] = a.y; ksv[nb][v0 + 2] = a.z; ksv[nb][v0 + 3] = a.w;
-            vsv[nb][v0] = b.x; vsv[nb][v0 + 1] = b.y; vsv[nb][v0 + 2] = b.z; vsv[nb][v0 + 3] = b.w;
-          }
+      for (int e = 0; e < 8; ++e) {
+        float x = sv[c][e];
+        if constexpr (kI8) x *= kv[e];   // K scale x softmax scale
+        if constexpr (kDiag) {
+          if (sc_off(c) + e > tlim) x = neg_inf();
         }
+        sv[c][e] = x;
+        cmax = fmaxf(cmax, x);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-
-    // scores: register v of half nb holds token 32 nb + (v % 8) + 8 h + 16 (v / 8) of the tile
-    const int tbase = it * kTile;
-    const bool diag = it >= first_diag;
-    float tmax = neg_inf();
+    // slots 4-7: exponentials of chunk c (the reference max first)
+    float corr = 1.f, mu = 0.f, rsum = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int tt = 32 * nb + (v & 7) + 8 * h + 16 * (v >> 3);
-        float sv;
-        if constexpr (kI8) sv = sacc[nb][v] * ksv[nb][v];   // k scale x softmax scale
-        else sv = sacc[nb][v] * p.scale_log2;
-        if (diag && tbase + tt > pos) sv = neg_inf();
-        sacc[nb][v] = sv;
-        tmax = fmaxf(tmax, sv);
+    for (int c = 0; c < 4; ++c) {
+      mfma2(4 + c);
+      if (c == 0) {
+        float tmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+        if constexpr (!kI8) tmax *= p.scale_log2;   // the max commutes with a positive scale
+        // move the reference max only when the tile exceeds it by more than
+        // the slack: weights stay below 2^kSlack and O is rarely rescaled
+        const bool need = tmax > m + kSlack;
+        corr = need ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;   // m = -inf -> 0
+        l *= corr;
+        m = need ? tmax : m;
+        mu = (m == neg_inf()) ? 0.f : m;
       }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    // move the reference max only when the tile exceeds it by more than the
-    // slack: weights stay below 2^kSlack and O is rarely rescaled
-    const bool need = tmax > m + kSlack;
-    if (wave_any(need)) {
-      const float mnew = need ? tmax : m;
-      const float corr = __builtin_amdgcn_exp2f(m - mnew);   // m = -inf -> 0; unchanged -> 1
-      l *= corr;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= corr;
-      m = mnew;
-    }
-    const float mu = (m == neg_inf()) ? 0.f : m;
-    float rsum = 0.f;
-    bf16x8_t phi[4], plo[4];   // P^T as a bf16 high part and a bf16 residual (~2^-17 together)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        // k-step 2 nb + half of the PV product: registers 8 half .. 8 half + 7
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int v = 8 * half + j;
-          float pv = __builtin_amdgcn_exp2f(sacc[nb][v] - mu);
-          rsum += pv;
-          if constexpr (kI8) pv *= vsv[nb][v];
-          const __bf16 hi = static_cast<__bf16>(pv);
-          phi[2 * nb + half][j] = hi;
-          plo[2 * nb + half][j] = static_cast<__bf16>(pv - static_cast<float>(hi));
-        }
+      float vv[8];
+      if constexpr (kI8) {
+        vv[0] = sc4[0].x; vv[1] = sc4[0].y; vv[2] = sc4[0].z; vv[3] = sc4[0].w;
+        vv[4] = sc4[1].x; vv[5] = sc4[1].y; vv[6] = sc4[1].z; vv[7] = sc4[1].w;
+        if (c < 3) read_sc(kTile + sc_off(c + 1));
       }
+      if (c == 3) {
+        // the first k-step's V operands of phase 2
+        const char* vb = s_kv[sv_stage];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) va0[db] = lds_read16(vb + vr_off[db][0]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float pw;
+        if constexpr (kI8) pw = __builtin_amdgcn_exp2f(sv[c][e] - mu);
+        else pw = __builtin_amdgcn_exp2f(fmaf(sv[c][e], p.scale_log2, -mu));
+        rsum += pw;
+        if constexpr (kI8) pw *= vv[e];
+        const __bf16 hi = static_cast<__bf16>(pw);
+        phi[c][e] = hi;
+        plo[c][e] = static_cast<__bf16>(pw - static_cast<float>(hi));
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     rsum += __shfl_xor(rsum, 32);
     l += rsum;
+    return corr;
+  };
 
-    // O^T += V^T P^T
+  auto phase2 = [&](int sv_stage, int st_stage, const bf16x8_t (&phi)[4], const bf16x8_t (&plo)[4],
+                    uint4 (&va0)[4], Staged& st, const TileSrc& ns) {
+    const char* vb = s_kv[sv_stage];
+    char* wb = s_kv[st_stage];
+    uint4 va[2][4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < 4; ++db) va[0][db] = va0[db];
+    uint32_t vw[4][4];
+    // slot s: k-step ks = s / 4; (s % 4) = high part of dims blocks 0,1 / 2,3,
+    // then the residual of 0,1 / 2,3
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(vb + vt_addr(32 * db + (lane & 31), 2 * ks + h));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), phi[ks], o[db], 0, 0, 0);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), plo[ks], o[db], 0, 0, 0);
+    for (int sl = 0; sl < 16; ++sl) {
+      const int ks = sl >> 2, q = sl & 3;
+      if (q == 0 && ks + 1 < 4) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) va[(ks + 1) & 1][db] = lds_read16(vb + vr_off[db][ks + 1]);
       }
+      const bf16x8_t b = (q < 2) ? phi[ks] : plo[ks];
+#pragma unroll
+      for (int d2 = 0; d2 < 2; ++d2) {
+        const int db = 2 * (q & 1) + d2;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va[ks & 1][db]), b, o[db], 0, 0, 0);
+      }
+      // staging of tile j + 2 (st -> LDS stage st_stage), then tile j + 4's loads
+      if (sl < 4) {
+        const int i = sl;
+        uint4 x = st.k[i];
+        if constexpr (kI8) {
+          x = make_uint4(i8pair_to_bf16x2(st.k[i].x, 0), i8pair_to_bf16x2(st.k[i].x, 2),
+                         i8pair_to_bf16x2(st.k[i].y, 0), i8pair_to_bf16x2(st.k[i].y, 2));
+        }
+        *reinterpret_cast<uint4*>(wb + kw_off + 4096 * i) = x;
+      } else if (sl < 8) {
+        const int i = sl - 4;
+        if constexpr (kI8) {
+          vw[i][0] = i8pair_to_bf16x2(st.v[i].x, 0);
+          vw[i][1] = i8pair_to_bf16x2(st.v[i].x, 2);
+          vw[i][2] = i8pair_to_bf16x2(st.v[i].y, 0);
+          vw[i][3] = i8pair_to_bf16x2(st.v[i].y, 2);
+        } else {
+          vw[i][0] = st.v[i].x;
+          vw[i][1] = st.v[i].y;
+          vw[i][2] = st.v[i].z;
+          vw[i][3] = st.v[i].w;
+        }
+      } else if (sl < 12) {
+        // transpose V: dims 8 u + e of tokens 4 tg .. 4 tg + 3, two dims per slot
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const int e = 2 * (sl - 8) + e2;
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t lo = __builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel);
+          const uint32_t hi = __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel);
+          *reinterpret_cast<uint2*>(wb + vw_off[e]) = make_uint2(lo, hi);
+        }
+      } else if (sl == 12) {
+        if constexpr (kI8) {
+          // threads t and t + 128 store the same value to the same place
+          const float sc = st.sc_ok ? st.sc : 0.f;
+          s_sc[st_stage][tid & (2 * kTile - 1)] = (tid & kTile) ? sc : sc * p.scale_log2;
+        }
+      } else if (sl == 13) {
+        gissue(ns, st);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
 
-    if (it + 1 < ntiles) lstore(buf ^ 1);
+  // ---- prologue: tiles 0 and 1 in LDS, tiles 2 and 3 in flight, S^T of tile 0 ----
+  Staged sa{}, sb{};
+  gload(0, sa);
+  gload(1, sb);
+  lstore(sa, 0);
+  lstore(sb, 1);
+  gload(2, sa);
+  gload(3, sb);
+  __syncthreads();
+  qk(0, sacc);
+
+  int st0 = 0;   // stage of tile j
+  auto iter = [&](auto diag_tag, int j, Staged& st) {
+    const int st1 = st0 == 2 ? 0 : st0 + 1;
+    const int st2 = st1 == 2 ? 0 : st1 + 1;
+    TileSrc nsrc;
+    tile_src(j + 4, nsrc);
+    bf16x8_t phi[4], plo[4];
+    f32x16_t snext[2];
+    uint4 va0[4];
+    __builtin_amdgcn_sched_barrier(0);
+    // S^T of tile j + 1 is garbage past the last tile (unused)
+    const float corr = phase1(diag_tag, j, st1, st0, snext, phi, plo, va0, st0);
+    if (wave_any(corr != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= corr;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // stage st2 receives stale data past the last tile (never read)
+    phase2(st0, st2, phi, plo, va0, st, nsrc);
     __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) sacc[nb] = snext[nb];
+    st0 = st1;
+  };
+  // tiles before the diagonal need no mask; the loops start at even tiles,
+  // so tile j always stages through register set j % 2
+  const int fd2 = min(first_diag, ntiles) & ~1;
+  int j = 0;
+  for (; j < fd2; j += 2) {
+    iter(std::false_type{}, j, sa);
+    iter(std::false_type{}, j + 1, sb);
+  }
+  for (; j < ntiles; j += 2) {
+    iter(std::true_type{}, j, sa);
+    if (j + 1 < ntiles) iter(std::true_type{}, j + 1, sb);
   }
 
   // ---- write: lane holds dims 32 db + 8 (v / 4) + 4 h + v % 4 of its row ----
