@@ -36,6 +36,12 @@ FLAGS = [
     "-I", INCLUDE,
     "-I", CSRC,
 ]
+# Per-source additions. The chunked-prefill kernel keeps its MFMA
+# accumulators in ordinary VGPRs, where its softmax reads them, instead of
+# copying them out of the accumulation registers every tile.
+EXTRA_FLAGS = {
+    "chunked.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc() -> str:
@@ -49,7 +55,7 @@ def sources() -> list[str]:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
