@@ -7,15 +7,19 @@
 // included) sit at positions n - L + r and attend keys t <= n - L + r;
 // softmax(scale * q . k) weighted values, online over 64-token KV tiles.
 //
-// Work mapping. A workgroup of 4 wavefronts owns one (sequence, kv head,
+// Work mapping. A workgroup of 8 wavefronts owns one (sequence, kv head,
 // query tile): 128 query rows = (128 / G) positions x the G query heads of the
-// GQA group, which all read the same K/V. Each wavefront owns 32 rows. Per
-// 64-token KV tile, with v_mfma_f32_32x32x16_bf16 (lane l of a 32x32 result
-// holds column l % 32 and rows 8(v/4) + 4(l/32) + v%4 of register v):
+// GQA group, which all read the same K/V. Wavefronts w and w + 4 own the same
+// 32 rows and split every KV tile: w takes its first 32 tokens, w + 4 the
+// other 32, each with its own online-softmax state; the two states merge once,
+// at the end, through LDS. Two wavefronts share each SIMD, so one's softmax
+// work issues while the other's MFMAs run. With v_mfma_f32_32x32x16_bf16
+// (lane l of a 32x32 result holds column l % 32 and rows 8(v/4) + 4(l/32) +
+// v%4 of register v), per 32-token half tile:
 //   S^T = K Q^T  (A = K rows from LDS, B = the wavefront's q rows, kept in
 //                 registers): every lane holds scores of ONE query row, so the
 //                 row max, the causal mask and the softmax state are lane-local
-//                 (the two lanes l, l^32 of a row hold its two token halves);
+//                 (the two lanes l, l^32 of a row hold its two token quarters);
 //   O^T = V^T P^T (A = V^T from LDS, B = P^T straight from the S^T registers,
 //                 as a bf16 high part plus a bf16 residual, two MFMAs: one
 //                 bf16 rounding of a weight (2^-9) is too coarse for rows that
@@ -28,9 +32,8 @@
 //
 // Pipeline. K is staged row-major and V transposed (the token index must be
 // the MFMA k dimension) in a ring of three LDS stages, XOR-swizzled against
-// bank conflicts. Iteration j runs two independent pairs of work, each in one
-// straight-line block, so that the wavefront's VALU work issues while its
-// MFMAs execute:
+// bank conflicts. Iteration j runs two phases, each written as slots of MFMAs
+// and a share of the VALU / LDS work, fenced so the interleaving survives:
 //   1. the softmax of tile j's scores  ||  S^T of tile j + 1 (MFMA);
 //   2. O^T += V_j^T P_j^T (MFMA)       ||  tile j + 2: registers -> LDS.
 // Global loads run two iterations ahead, into two register sets, as buffer
@@ -57,7 +60,7 @@ typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;            // head_dim built
 constexpr int kRows = 128;         // query rows per workgroup
 constexpr int kTile = 64;          // tokens per KV tile
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kXcdsC = 8;
 constexpr int kStages = 3;
 constexpr int kKBytes = kTile * kD * 2;    // 16 KiB, row-major [token][dim], swizzled
@@ -65,6 +68,7 @@ constexpr int kVBytes = kD * kTile * 2;    // 16 KiB, transposed [dim][token], s
 constexpr int kStageBytes = kKBytes + kVBytes;
 constexpr int kIdsCached = 4096;           // block ids kept in LDS (65536 tokens)
 constexpr int kRsrcWord3 = 0x00020000;     // buffer descriptor word 3 (gfx9 family): raw dwords
+constexpr int kMergeFloats = 66;           // per lane of a merging wavefront: o[64], m, l
 
 // Row order of the S^T product: bits 2 and 3 of the row index swapped.
 __device__ __forceinline__ int sigma(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
@@ -93,11 +97,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int byt
 
 __device__ __forceinline__ uint4 lds_read16(const char* a) { return *reinterpret_cast<const uint4*>(a); }
 
-// One tile's global loads, held in registers until they are stored to LDS.
+// One tile's global loads for one thread, held in registers until they are
+// stored to LDS. tg = thread / 16 (0 .. 31), u = thread % 16.
 struct Staged {
-  uint4 k[4];      // K chunk i: block i, row thread / 16, 16-byte unit thread % 16
-  uint4 v[4];      // V chunk i: block w, row 4 (tg % 4) + i, same unit
-  float sc;        // int8: one K (thread % 128 < 64) or V scale of the tile
+  uint4 k[2];      // K chunk i: token tg + 32 i, 16-byte unit u (int8: 8 bytes)
+  uint4 v[2];      // V: tokens 2 tg and 2 tg + 1, unit u
+  float sc;        // int8: the K (thread % 128 < 64) or V scale of token thread % 64
   bool sc_ok;      // that token exists
 };
 
@@ -107,9 +112,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   constexpr bool kI8 = (KV == PKV_I8);
   constexpr float kSlack = 8.0f;
   constexpr int kRowBytes = kI8 ? kD : 2 * kD;   // bytes of one cached K or V row
+  constexpr int kUnit = kRowBytes / 16;          // bytes of 8 dims of a cached row
   __shared__ __attribute__((aligned(16))) char s_kv[kStages][kStageBytes];
   __shared__ __attribute__((aligned(16))) float s_sc[kStages][2 * kTile];   // int8: K scale x softmax scale, V scale
   __shared__ __attribute__((aligned(16))) int s_ids[kIdsCached];
+  static_assert(kStages * kStageBytes >= 4 * kMergeFloats * 64 * 4, "merge area");
 
   // ---- work item: (sequence, kv head, query tile), XCD-contiguous ----
   const int QT = (p.max_q_len + P - 1) / P;
@@ -123,8 +130,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int h = lane >> 5;                          // which token half of a row this lane holds
-  const int rrow = 32 * w + (lane & 31);            // row of the 128-row tile
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int rb = wu & 3;                            // row block of this wavefront
+  const int th = wu >> 2;                           // which 32-token half of each tile
+  const int h = lane >> 5;                          // which token quarter of that half a lane holds
+  const int rrow = 32 * rb + (lane & 31);           // row of the 128-row tile
   const int g = rrow / P;
   const int pi = qt * P + rrow % P;                 // row index within the chunk
 
@@ -207,18 +217,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   };
 
   const int u16 = tid & 15;
-  const int tg = tid >> 4;
+  const int tg = tid >> 4;                          // 0 .. 31; tg / 4 == wavefront
   const char* kpool = static_cast<const char*>(p.k);
   const char* vpool = static_cast<const char*>(p.v);
-  const int wu = __builtin_amdgcn_readfirstlane(w);
 
   // Where tile `tile`'s loads come from: buffer descriptors over the valid
-  // rows of its blocks (none for blocks the range does not need), and this
-  // thread's scale. Any tile index is safe.
+  // rows of this wavefront's blocks (none for blocks the range does not
+  // need) and this thread's scale. K chunks come from blocks th and th + 2,
+  // V from block w / 2. Any tile index is safe.
   struct TileSrc {
-    __amdgpu_buffer_rsrc_t k[4];   // block i of the tile
-    __amdgpu_buffer_rsrc_t v;      // block w: this wavefront's V rows
-    const float* sc;               // int8: K scale (thread % 128 < 64) or V scale of token thread % 64
+    __amdgpu_buffer_rsrc_t k[2];
+    __amdgpu_buffer_rsrc_t v;
+    const float* sc;
     bool sc_ok;
   };
   const float* sc_pool = (tid & kTile) ? p.v_scale : p.k_scale;
@@ -231,16 +241,21 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     for (int bi = 0; bi < 4; ++bi) {
       rows[bi] = ((ok >> bi) & 1u) ? min(kBlock, n - (blk0 + bi) * kBlock) : 0;   // valid rows of block bi
       id[bi] = ((ok >> bi) & 1u) ? id[bi] : 0;
-      ts.k[bi] = rsrc(kpool + (static_cast<size_t>(id[bi]) * p.num_kv_heads + kh) * kBlock * kRowBytes,
-                      rows[bi] * kRowBytes);
     }
-    int idw = id[0], roww = rows[0];
+    const int bk0 = th, bk1 = th + 2, bv = wu >> 1;
+    const int idk0 = bk0 == 0 ? id[0] : id[1], rk0 = bk0 == 0 ? rows[0] : rows[1];
+    const int idk1 = bk1 == 2 ? id[2] : id[3], rk1 = bk1 == 2 ? rows[2] : rows[3];
+    int idv = id[0], rv = rows[0];
 #pragma unroll
     for (int bi = 1; bi < 4; ++bi) {
-      idw = wu == bi ? id[bi] : idw;
-      roww = wu == bi ? rows[bi] : roww;
+      idv = bv == bi ? id[bi] : idv;
+      rv = bv == bi ? rows[bi] : rv;
     }
-    ts.v = rsrc(vpool + (static_cast<size_t>(idw) * p.num_kv_heads + kh) * kBlock * kRowBytes, roww * kRowBytes);
+    const size_t head_off = static_cast<size_t>(kh) * kBlock * kRowBytes;
+    const size_t blk_stride = static_cast<size_t>(p.num_kv_heads) * kBlock * kRowBytes;
+    ts.k[0] = rsrc(kpool + head_off + idk0 * blk_stride, rk0 * kRowBytes);
+    ts.k[1] = rsrc(kpool + head_off + idk1 * blk_stride, rk1 * kRowBytes);
+    ts.v = rsrc(vpool + head_off + idv * blk_stride, rv * kRowBytes);
     if constexpr (kI8) {
       const int tt = tid & (kTile - 1);
       const int bs = tt >> 4;
@@ -254,30 +269,24 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       ts.sc = sc_pool + (static_cast<size_t>(ids) * p.num_kv_heads + kh) * kBlock + (tt & 15);
     }
   };
-  // The loads themselves: the same 8 (+1 scale) loads for every tile, no branch.
-  const int koff = tg * kRowBytes + u16 * (kRowBytes / 16);             // K chunk i: row tg of block i
-  const int voff = 4 * (tg & 3) * kRowBytes + u16 * (kRowBytes / 16);   // V chunk i: row 4 (tg % 4) + i of block w
+  // The loads themselves: the same 4 (+1 scale) loads for every tile, no branch.
+  const int koff = (tg & 15) * kRowBytes + u16 * kUnit;            // K chunk i: row tg % 16 of block th + 2 i
+  const int voff = ((2 * tg) & 15) * kRowBytes + u16 * kUnit;      // V: rows 2 tg % 16, + 1 of block w / 2
   auto gissue = [&](const TileSrc& ts, Staged& st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       if constexpr (kI8) {
         const u32x2v_t c = __builtin_bit_cast(u32x2v_t, __builtin_amdgcn_raw_buffer_load_b64(ts.k[i], koff, 0, 0));
         st.k[i] = make_uint4(c.x, c.y, 0, 0);
+        const u32x2v_t d = __builtin_bit_cast(
+            u32x2v_t, __builtin_amdgcn_raw_buffer_load_b64(ts.v, voff + i * kRowBytes, 0, 0));
+        st.v[i] = make_uint4(d.x, d.y, 0, 0);
       } else {
         const u32x4v_t c = __builtin_bit_cast(u32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(ts.k[i], koff, 0, 0));
         st.k[i] = make_uint4(c.x, c.y, c.z, c.w);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (kI8) {
-        const u32x2v_t c = __builtin_bit_cast(
-            u32x2v_t, __builtin_amdgcn_raw_buffer_load_b64(ts.v, voff + i * kRowBytes, 0, 0));
-        st.v[i] = make_uint4(c.x, c.y, 0, 0);
-      } else {
-        const u32x4v_t c = __builtin_bit_cast(
+        const u32x4v_t d = __builtin_bit_cast(
             u32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(ts.v, voff + i * kRowBytes, 0, 0));
-        st.v[i] = make_uint4(c.x, c.y, c.z, c.w);
+        st.v[i] = make_uint4(d.x, d.y, d.z, d.w);
       }
     }
     if constexpr (kI8) {
@@ -292,26 +301,23 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   };
 
   // LDS byte offsets of this thread's stores, the same for every stage
-  const int kw_off = k_off(tg, u16);                // K chunk i: token 16 i + tg, + 4096 i
-  int vw_off[8];                                    // V^T dim 8 u + e, tokens 4 tg .. +3
-#pragma unroll
-  for (int e = 0; e < 8; ++e) vw_off[e] = kKBytes + vt_off(8 * u16 + e, tg >> 1) + ((tg & 1) << 3);
+  const int kw_off = k_off(tg, u16);                 // K chunk i: token tg + 32 i, + 8192 i
+  // V^T: dims 8 u + e, tokens 2 tg, 2 tg + 1 (4 bytes in unit tg / 4)
+  auto vw_off = [&](int e) { return kKBytes + vt_off(8 * u16 + e, tg >> 2) + ((tg & 3) << 2); };
 
-  auto lstore = [&](const Staged& st, int stage) {
-    char* sb = s_kv[stage];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint4 x = st.k[i];
-      if constexpr (kI8) {
-        x = make_uint4(i8pair_to_bf16x2(st.k[i].x, 0), i8pair_to_bf16x2(st.k[i].x, 2),
-                       i8pair_to_bf16x2(st.k[i].y, 0), i8pair_to_bf16x2(st.k[i].y, 2));
-      }
-      *reinterpret_cast<uint4*>(sb + kw_off + 4096 * i) = x;
+  // K chunk i of st -> bf16 (int8 codes converted)
+  auto k_bf16 = [&](const Staged& st, int i) -> uint4 {
+    if constexpr (kI8) {
+      return make_uint4(i8pair_to_bf16x2(st.k[i].x, 0), i8pair_to_bf16x2(st.k[i].x, 2),
+                        i8pair_to_bf16x2(st.k[i].y, 0), i8pair_to_bf16x2(st.k[i].y, 2));
+    } else {
+      return st.k[i];
     }
-    // transpose V: thread holds tokens 4 tg .. 4 tg + 3 of dims 8 u .. 8 u + 7
-    uint32_t vw[4][4];
+  };
+  // the two V tokens of st as bf16 words: vw[i][k] = dims 8 u + 2k, +1 of token 2 tg + i
+  auto v_bf16 = [&](const Staged& st, uint32_t (&vw)[2][4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       if constexpr (kI8) {
         vw[i][0] = i8pair_to_bf16x2(st.v[i].x, 0);
         vw[i][1] = i8pair_to_bf16x2(st.v[i].x, 2);
@@ -324,124 +330,114 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
         vw[i][3] = st.v[i].w;
       }
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // dim 8 u + e of the 4 tokens: low or high half of word e / 2 of each token
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t lo = __builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel);
-      const uint32_t hi = __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel);
-      *reinterpret_cast<uint2*>(sb + vw_off[e]) = make_uint2(lo, hi);
-    }
+  };
+  // dim 8 u + e of tokens 2 tg, 2 tg + 1, packed
+  auto v_pair = [&](const uint32_t (&vw)[2][4], int e) -> uint32_t {
+    return __builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+  };
+  auto sc_store = [&](const Staged& st, int stage) {
     if constexpr (kI8) {
-      // threads t and t + 128 store the same value to the same place
+      // threads t, t + 128, t + 256, t + 384 store the same value to the same place
       const float sc = st.sc_ok ? st.sc : 0.f;
       s_sc[stage][tid & (2 * kTile - 1)] = (tid & kTile) ? sc : sc * p.scale_log2;
     }
   };
+  auto lstore = [&](const Staged& st, int stage) {
+    char* sb = s_kv[stage];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(sb + kw_off + 8192 * i) = k_bf16(st, i);
+    uint32_t vw[2][4];
+    v_bf16(st, vw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(sb + vw_off(e)) = v_pair(vw, e);
+    sc_store(st, stage);
+  };
 
   // LDS byte offsets of this lane's MFMA operand reads, the same for every stage
   const int ar = lane & 31;
-  int kr_off[8];                                    // K row sigma(ar) (+ 32 rows: + 8192), unit 2 ks + h
+  int kr_off[8];                                    // K row 32 th + sigma(ar), unit 2 ks + h
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) kr_off[ks] = k_off(sigma(ar), 2 * ks + h);
-  int vr_off[4][4];                                 // V^T row 32 db + ar, unit 2 ks + h
+  for (int ks = 0; ks < 8; ++ks) kr_off[ks] = k_off(32 * th + sigma(ar), 2 * ks + h);
+  int vr_off[4][2];                                 // V^T row 32 db + ar, unit 2 (2 th + k2) + h
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) vr_off[db][ks] = kKBytes + vt_off(32 * db + ar, 2 * ks + h);
+    for (int k2 = 0; k2 < 2; ++k2) vr_off[db][k2] = kKBytes + vt_off(32 * db + ar, 2 * (2 * th + k2) + h);
   }
 
-  // S^T of the tile in `stage`, for its two 32-token halves
-  auto qk = [&](int stage, f32x16_t (&s)[2]) {
+  // S^T of this wavefront's half of the tile in `stage`
+  auto qk = [&](int stage, f32x16_t& s) {
     const char* kb = s_kv[stage];
-    s[0] = f32x16_t{};
-    s[1] = f32x16_t{};
+    s = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const uint4 a0 = lds_read16(kb + kr_off[ks]);
-      const uint4 a1 = lds_read16(kb + kr_off[ks] + 8192);
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), qb[ks], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), qb[ks], s[1], 0, 0, 0);
+      const uint4 a = lds_read16(kb + kr_off[ks]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qb[ks], s, 0, 0, 0);
     }
   };
 
-  // ---- online softmax state of this lane's row ----
+  // ---- online softmax state of this lane's row, over this wavefront's tokens ----
   float m = neg_inf(), l = 0.f;
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
-  f32x16_t sacc[2];   // S^T of the tile being softmaxed
+  f32x16_t sacc;   // S^T of the tile being softmaxed
 
-  // Iteration j: phase 1 = softmax of tile j || S^T of tile j + 1; phase 2 =
-  // O^T += V_j^T P_j^T || tile j + 2 from registers to LDS, tile j + 4's
-  // loads. Each phase is written as slots of two MFMAs plus a share of the
-  // VALU / LDS work, fenced so the compiler keeps the interleaving; operand
-  // reads run ahead of their MFMAs, and MFMAs on the same accumulator are
-  // never adjacent.
-  auto phase1 = [&](auto diag_tag, int j, int sk, int ss, f32x16_t (&sn)[2], bf16x8_t (&phi)[4],
-                    bf16x8_t (&plo)[4], uint4 (&va0)[4], int sv_stage) -> float {
+  // scores: register v of the wavefront's half holds token
+  // 32 th + 8 h + 16 (v / 8) + (v % 8) of the tile; chunk c = v / 4
+  auto tok_of = [&](int v) { return 32 * th + 8 * h + 16 * (v >> 3) + (v & 7); };
+
+  // Phase 1: softmax of tile j (scores in sacc, scales in stage ss) || S^T
+  // of tile j + 1 (K in stage sk) into sn, in 8 slots of one MFMA.
+  auto phase1 = [&](auto diag_tag, int j, int sk, int ss, f32x16_t& sn, bf16x8_t (&phi)[2], bf16x8_t (&plo)[2],
+                    uint4 (&va0)[4], int sv_stage) -> float {
     constexpr bool kDiag = decltype(diag_tag)::value;
-    const char* kb = s_kv[sk];            // K of tile j + 1
-    const float* scs = s_sc[ss];          // int8 scales of tile j
+    const char* kb = s_kv[sk];
+    const float* scs = s_sc[ss];
     const int tlim = pos - j * kTile;     // tile tokens past this one are masked
-    uint4 ka[3][2];
-    auto read_k = [&](int ks, uint4 (&dst)[2]) {
-      dst[0] = lds_read16(kb + kr_off[ks]);
-      dst[1] = lds_read16(kb + kr_off[ks] + 8192);
-    };
-    // scores of chunk c = (half nb = c / 2, registers 8 (c % 2) .. + 7):
-    // tokens 32 nb + 8 h + 16 (c % 2) + e, e = 0 .. 7
-    auto sc_off = [&](int c) { return 32 * (c >> 1) + 8 * h + 16 * (c & 1); };
-    float4 sc4[2];
-    auto read_sc = [&](int off) {
-      sc4[0] = *reinterpret_cast<const float4*>(scs + off);
-      sc4[1] = *reinterpret_cast<const float4*>(scs + off + 4);
-    };
-    read_k(0, ka[0]);
-    read_k(1, ka[1]);
-    read_k(2, ka[2]);
-    if constexpr (kI8) read_sc(sc_off(0));
-    float sv[4][8];
+    uint4 ka[3];
+    ka[0] = lds_read16(kb + kr_off[0]);
+    ka[1] = lds_read16(kb + kr_off[1]);
+    ka[2] = lds_read16(kb + kr_off[2]);
+    float4 sc4;
+    auto read_sc = [&](int t0) { sc4 = *reinterpret_cast<const float4*>(scs + t0); };
+    if constexpr (kI8) read_sc(tok_of(0));
+    float sv[16];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sv[c][e] = sacc[c >> 1][8 * (c & 1) + e];
-    }
-    sn[0] = f32x16_t{};
-    sn[1] = f32x16_t{};
-    auto mfma2 = [&](int ks) {
-      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks % 3][0]), qb[ks], sn[0], 0, 0, 0);
-      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks % 3][1]), qb[ks], sn[1], 0, 0, 0);
-      if (ks + 3 < 8) read_k(ks + 3, ka[ks % 3]);
+    for (int v = 0; v < 16; ++v) sv[v] = sacc[v];
+    sn = f32x16_t{};
+    auto mfma1 = [&](int ks) {
+      sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks % 3]), qb[ks], sn, 0, 0, 0);
+      if (ks + 3 < 8) ka[ks % 3] = lds_read16(kb + kr_off[ks + 3]);
     };
-    // slots 0-3: scale, mask and max of chunk c
+    // slots 0-3: scale, mask and max of scores 4 c .. 4 c + 3
     float cmax = neg_inf();
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      mfma2(c);
-      float kv[8];
+      mfma1(c);
+      float kv[4];
       if constexpr (kI8) {
-        kv[0] = sc4[0].x; kv[1] = sc4[0].y; kv[2] = sc4[0].z; kv[3] = sc4[0].w;
-        kv[4] = sc4[1].x; kv[5] = sc4[1].y; kv[6] = sc4[1].z; kv[7] = sc4[1].w;
-        read_sc(c < 3 ? sc_off(c + 1) : kTile + sc_off(0));   // next: K scales of chunk c + 1, then V of chunk 0
+        kv[0] = sc4.x; kv[1] = sc4.y; kv[2] = sc4.z; kv[3] = sc4.w;
+        read_sc(c < 3 ? tok_of(4 * (c + 1)) : kTile + tok_of(0));   // next: K scales, then V scales of scores 0..3
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = sv[c][e];
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * c + e;
+        float x = sv[v];
         if constexpr (kI8) x *= kv[e];   // K scale x softmax scale
         if constexpr (kDiag) {
-          if (sc_off(c) + e > tlim) x = neg_inf();
+          if (tok_of(v) > tlim) x = neg_inf();
         }
-        sv[c][e] = x;
+        sv[v] = x;
         cmax = fmaxf(cmax, x);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // slots 4-7: exponentials of chunk c (the reference max first)
+    // slots 4-7: exponentials of scores 4 c .. 4 c + 3 (the reference max first)
     float corr = 1.f, mu = 0.f, rsum = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      mfma2(4 + c);
+      mfma1(4 + c);
       if (c == 0) {
         float tmax = fmaxf(cmax, __shfl_xor(cmax, 32));
         if constexpr (!kI8) tmax *= p.scale_log2;   // the max commutes with a positive scale
@@ -453,11 +449,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
         m = need ? tmax : m;
         mu = (m == neg_inf()) ? 0.f : m;
       }
-      float vv[8];
+      float vv[4];
       if constexpr (kI8) {
-        vv[0] = sc4[0].x; vv[1] = sc4[0].y; vv[2] = sc4[0].z; vv[3] = sc4[0].w;
-        vv[4] = sc4[1].x; vv[5] = sc4[1].y; vv[6] = sc4[1].z; vv[7] = sc4[1].w;
-        if (c < 3) read_sc(kTile + sc_off(c + 1));
+        vv[0] = sc4.x; vv[1] = sc4.y; vv[2] = sc4.z; vv[3] = sc4.w;
+        if (c < 3) read_sc(kTile + tok_of(4 * (c + 1)));
       }
       if (c == 3) {
         // the first k-step's V operands of phase 2
@@ -466,15 +461,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
         for (int db = 0; db < 4; ++db) va0[db] = lds_read16(vb + vr_off[db][0]);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * c + e;
         float pw;
-        if constexpr (kI8) pw = __builtin_amdgcn_exp2f(sv[c][e] - mu);
-        else pw = __builtin_amdgcn_exp2f(fmaf(sv[c][e], p.scale_log2, -mu));
+        if constexpr (kI8) pw = __builtin_amdgcn_exp2f(sv[v] - mu);
+        else pw = __builtin_amdgcn_exp2f(fmaf(sv[v], p.scale_log2, -mu));
         rsum += pw;
         if constexpr (kI8) pw *= vv[e];
         const __bf16 hi = static_cast<__bf16>(pw);
-        phi[c][e] = hi;
-        plo[c][e] = static_cast<__bf16>(pw - static_cast<float>(hi));
+        phi[v >> 3][v & 7] = hi;
+        plo[v >> 3][v & 7] = static_cast<__bf16>(pw - static_cast<float>(hi));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -483,68 +479,45 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     return corr;
   };
 
-  auto phase2 = [&](int sv_stage, int st_stage, const bf16x8_t (&phi)[4], const bf16x8_t (&plo)[4],
+  // Phase 2: O^T += V^T P^T over this wavefront's 32 tokens (V in stage
+  // sv_stage) || tile j + 2 from st to stage st_stage, then tile j + 4's
+  // loads into st; 8 slots of two MFMAs on different accumulators.
+  auto phase2 = [&](int sv_stage, int st_stage, const bf16x8_t (&phi)[2], const bf16x8_t (&plo)[2],
                     uint4 (&va0)[4], Staged& st, const TileSrc& ns) {
     const char* vb = s_kv[sv_stage];
     char* wb = s_kv[st_stage];
     uint4 va[2][4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) va[0][db] = va0[db];
-    uint32_t vw[4][4];
-    // slot s: k-step ks = s / 4; (s % 4) = high part of dims blocks 0,1 / 2,3,
+    uint32_t vw[2][4];
+    // slot s: k-step k2 = s / 4; (s % 4) = high part of dims blocks 0,1 / 2,3,
     // then the residual of 0,1 / 2,3
 #pragma unroll
-    for (int sl = 0; sl < 16; ++sl) {
-      const int ks = sl >> 2, q = sl & 3;
-      if (q == 0 && ks + 1 < 4) {
+    for (int sl = 0; sl < 8; ++sl) {
+      const int k2 = sl >> 2, q = sl & 3;
+      if (sl == 0) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) va[(ks + 1) & 1][db] = lds_read16(vb + vr_off[db][ks + 1]);
+        for (int db = 0; db < 4; ++db) va[1][db] = lds_read16(vb + vr_off[db][1]);
       }
-      const bf16x8_t b = (q < 2) ? phi[ks] : plo[ks];
+      const bf16x8_t b = (q < 2) ? phi[k2] : plo[k2];
 #pragma unroll
       for (int d2 = 0; d2 < 2; ++d2) {
         const int db = 2 * (q & 1) + d2;
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va[ks & 1][db]), b, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va[k2][db]), b, o[db], 0, 0, 0);
       }
       // staging of tile j + 2 (st -> LDS stage st_stage), then tile j + 4's loads
-      if (sl < 4) {
-        const int i = sl;
-        uint4 x = st.k[i];
-        if constexpr (kI8) {
-          x = make_uint4(i8pair_to_bf16x2(st.k[i].x, 0), i8pair_to_bf16x2(st.k[i].x, 2),
-                         i8pair_to_bf16x2(st.k[i].y, 0), i8pair_to_bf16x2(st.k[i].y, 2));
-        }
-        *reinterpret_cast<uint4*>(wb + kw_off + 4096 * i) = x;
-      } else if (sl < 8) {
-        const int i = sl - 4;
-        if constexpr (kI8) {
-          vw[i][0] = i8pair_to_bf16x2(st.v[i].x, 0);
-          vw[i][1] = i8pair_to_bf16x2(st.v[i].x, 2);
-          vw[i][2] = i8pair_to_bf16x2(st.v[i].y, 0);
-          vw[i][3] = i8pair_to_bf16x2(st.v[i].y, 2);
-        } else {
-          vw[i][0] = st.v[i].x;
-          vw[i][1] = st.v[i].y;
-          vw[i][2] = st.v[i].z;
-          vw[i][3] = st.v[i].w;
-        }
-      } else if (sl < 12) {
-        // transpose V: dims 8 u + e of tokens 4 tg .. 4 tg + 3, two dims per slot
+      if (sl < 2) {
+        *reinterpret_cast<uint4*>(wb + kw_off + 8192 * sl) = k_bf16(st, sl);
+      } else if (sl == 2) {
+        v_bf16(st, vw);
+      } else if (sl < 7) {
 #pragma unroll
         for (int e2 = 0; e2 < 2; ++e2) {
-          const int e = 2 * (sl - 8) + e2;
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const uint32_t lo = __builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel);
-          const uint32_t hi = __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel);
-          *reinterpret_cast<uint2*>(wb + vw_off[e]) = make_uint2(lo, hi);
+          const int e = 2 * (sl - 3) + e2;
+          *reinterpret_cast<uint32_t*>(wb + vw_off(e)) = v_pair(vw, e);
         }
-      } else if (sl == 12) {
-        if constexpr (kI8) {
-          // threads t and t + 128 store the same value to the same place
-          const float sc = st.sc_ok ? st.sc : 0.f;
-          s_sc[st_stage][tid & (2 * kTile - 1)] = (tid & kTile) ? sc : sc * p.scale_log2;
-        }
-      } else if (sl == 13) {
+      } else {
+        sc_store(st, st_stage);
         gissue(ns, st);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -568,8 +541,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     const int st2 = st1 == 2 ? 0 : st1 + 1;
     TileSrc nsrc;
     tile_src(j + 4, nsrc);
-    bf16x8_t phi[4], plo[4];
-    f32x16_t snext[2];
+    bf16x8_t phi[2], plo[2];
+    f32x16_t snext;
     uint4 va0[4];
     __builtin_amdgcn_sched_barrier(0);
     // S^T of tile j + 1 is garbage past the last tile (unused)
@@ -582,8 +555,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     // stage st2 receives stale data past the last tile (never read)
     phase2(st0, st2, phi, plo, va0, st, nsrc);
     __syncthreads();
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) sacc[nb] = snext[nb];
+    sacc = snext;
     st0 = st1;
   };
   // tiles before the diagonal need no mask; the loops start at even tiles,
@@ -599,22 +571,45 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     if (j + 1 < ntiles) iter(std::true_type{}, j + 1, sb);
   }
 
+  // ---- merge the two token halves: wavefront w + 4 hands (o, m, l) to w ----
+  bad = __syncthreads_or(bad);   // also: every wavefront is done with the stages
+  float* mb = reinterpret_cast<float*>(&s_kv[0][0]) + (rb * kMergeFloats) * 64 + lane;   // [rb][66][64 lanes]
+  if (th == 1) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mb[(16 * db + v) * 64] = o[db][v];
+    }
+    mb[64 * 64] = m;
+    mb[65 * 64] = l;
+  }
+  __syncthreads();
+  if (th == 1 || !row_live) return;
+  const float m2 = mb[64 * 64], l2 = mb[65 * 64];
+  const float mm = fmaxf(m, m2);
+  const float a1 = (m == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+  const float a2 = (m2 == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
+  const float lt = l * a1 + l2 * a2;
+  const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+
   // ---- write: lane holds dims 32 db + 8 (v / 4) + 4 h + v % 4 of its row ----
-  bad = __syncthreads_or(bad);
-  if (!row_live) return;
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
-      float4 x = make_float4(o[db][4 * v4] * inv, o[db][4 * v4 + 1] * inv, o[db][4 * v4 + 2] * inv,
-                             o[db][4 * v4 + 3] * inv);
+      float y[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int v = 4 * v4 + k;
+        y[k] = (o[db][v] * a1 + mb[(16 * db + v) * 64] * a2) * inv;
+      }
+      float4 x = make_float4(y[0], y[1], y[2], y[3]);
       if (bad) x = make_float4(qnan(), qnan(), qnan(), qnan());
       *reinterpret_cast<float4*>(out_row + 32 * db + 8 * v4 + 4 * h) = x;
     }
   }
   if (h == 0 && p.lse != nullptr) {
-    const float lse = bad ? qnan() : (l > 0.f ? (m + log2f(l)) * kLn2 : neg_inf());
+    const float lse = bad ? qnan() : (lt > 0.f ? (mm + log2f(lt)) * kLn2 : neg_inf());
     p.lse[static_cast<size_t>(q0 + pi) * p.num_q_heads + hq] = lse;
   }
 }
