@@ -98,11 +98,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int byt
 __device__ __forceinline__ uint4 lds_read16(const char* a) { return *reinterpret_cast<const uint4*>(a); }
 
 // One tile's global loads for one thread, held in registers until they are
-// stored to LDS. tg = thread / 16 (0 .. 31), u = thread % 16.
+// stored to LDS. A thread stages part of its group's 32-token half of the
+// tile: tg = (thread % 256) / 16, u = thread % 16.
 struct Staged {
-  uint4 k[2];      // K chunk i: token tg + 32 i, 16-byte unit u (int8: 8 bytes)
-  uint4 v[2];      // V: tokens 2 tg and 2 tg + 1, unit u
-  float sc;        // int8: the K (thread % 128 < 64) or V scale of token thread % 64
+  uint4 k[2];      // K chunk i: token tg + 16 i of the half, 16-byte unit u (int8: 8 bytes)
+  uint4 v[2];      // V: tokens 2 tg and 2 tg + 1 of the half, unit u
+  float sc;        // int8: the K (thread % 64 < 32) or V scale of token thread % 32 of the half
   bool sc_ok;      // that token exists
 };
 
@@ -191,87 +192,67 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   for (int j = tid; j < min(nblk_need, kIdsCached); j += kThreads) s_ids[j] = trow[j];
   __syncthreads();
 
-  // Block ids of the 4 blocks of a tile (uniform), read before any of the
-  // tile's loads are issued. ok bit bi: block bi is one this tile range needs
-  // and its id is inside the pool; a needed id outside the pool poisons the
-  // output instead.
-  auto tile_ids = [&](int tile, int (&id)[4]) -> unsigned {
-    const int blk0 = tile * (kTile / kBlock);
-    if (blk0 + 4 <= kIdsCached) {
-      const int4 x = *reinterpret_cast<const int4*>(&s_ids[blk0]);
-      id[0] = x.x; id[1] = x.y; id[2] = x.z; id[3] = x.w;
-    } else {
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi) id[bi] = blk0 + bi < nblk_need ? trow[blk0 + bi] : 0;
-    }
-    unsigned ok = 0;
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-      id[bi] = __builtin_amdgcn_readfirstlane(id[bi]);
-      if (blk0 + bi < nblk_need) {
-        if (static_cast<unsigned>(id[bi]) < static_cast<unsigned>(p.num_blocks)) ok |= 1u << bi;
-        else bad = 1;
-      }
-    }
-    return ok;
-  };
-
-  const int u16 = tid & 15;
-  const int tg = tid >> 4;                          // 0 .. 31; tg / 4 == wavefront
+  // Each group of 4 wavefronts (th = 0: wavefronts 0-3, th = 1: 4-7) loads
+  // and stages only the 32-token half of every tile it computes on, so the
+  // two groups share no staged data. Group-local thread tl: tg = tl / 16
+  // (0 .. 15), u = tl % 16.
+  const int tl = tid & 255;
+  const int u16 = tl & 15;
+  const int tg = tl >> 4;
+  const int wl = wu & 3;                            // wavefront within its group
   const char* kpool = static_cast<const char*>(p.k);
   const char* vpool = static_cast<const char*>(p.v);
 
   // Where tile `tile`'s loads come from: buffer descriptors over the valid
   // rows of this wavefront's blocks (none for blocks the range does not
-  // need) and this thread's scale. K chunks come from blocks th and th + 2,
-  // V from block w / 2. Any tile index is safe.
+  // need) and this thread's scale. K chunk i comes from block 2 th + i
+  // (row tg), V from block 2 th + wl / 2. Any tile index is safe.
   struct TileSrc {
     __amdgpu_buffer_rsrc_t k[2];
     __amdgpu_buffer_rsrc_t v;
     const float* sc;
     bool sc_ok;
   };
-  const float* sc_pool = (tid & kTile) ? p.v_scale : p.k_scale;
-  auto tile_src = [&](int tile, TileSrc& ts) {
-    int id[4];
-    const unsigned ok = tile_ids(tile, id);
-    const int blk0 = tile * (kTile / kBlock);
-    int rows[4];
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-      rows[bi] = ((ok >> bi) & 1u) ? min(kBlock, n - (blk0 + bi) * kBlock) : 0;   // valid rows of block bi
-      id[bi] = ((ok >> bi) & 1u) ? id[bi] : 0;
-    }
-    const int bk0 = th, bk1 = th + 2, bv = wu >> 1;
-    const int idk0 = bk0 == 0 ? id[0] : id[1], rk0 = bk0 == 0 ? rows[0] : rows[1];
-    const int idk1 = bk1 == 2 ? id[2] : id[3], rk1 = bk1 == 2 ? rows[2] : rows[3];
-    int idv = id[0], rv = rows[0];
-#pragma unroll
-    for (int bi = 1; bi < 4; ++bi) {
-      idv = bv == bi ? id[bi] : idv;
-      rv = bv == bi ? rows[bi] : rv;
-    }
-    const size_t head_off = static_cast<size_t>(kh) * kBlock * kRowBytes;
-    const size_t blk_stride = static_cast<size_t>(p.num_kv_heads) * kBlock * kRowBytes;
-    ts.k[0] = rsrc(kpool + head_off + idk0 * blk_stride, rk0 * kRowBytes);
-    ts.k[1] = rsrc(kpool + head_off + idk1 * blk_stride, rk1 * kRowBytes);
-    ts.v = rsrc(vpool + head_off + idv * blk_stride, rv * kRowBytes);
-    if constexpr (kI8) {
-      const int tt = tid & (kTile - 1);
-      const int bs = tt >> 4;
-      int ids = id[0], rws = rows[0];
-#pragma unroll
-      for (int bi = 1; bi < 4; ++bi) {
-        ids = bs == bi ? id[bi] : ids;
-        rws = bs == bi ? rows[bi] : rws;
+  const float* sc_pool = (tl & 32) ? p.v_scale : p.k_scale;
+  const size_t head_off = static_cast<size_t>(kh) * kBlock * kRowBytes;
+  const size_t blk_stride = static_cast<size_t>(p.num_kv_heads) * kBlock * kRowBytes;
+  // block blk of the sequence: its id (0 if the range does not need it, or
+  // it is outside the pool, which poisons the output) and its valid rows
+  auto block_src = [&](int blk, int& rows) -> int {
+    int id = 0;
+    rows = 0;
+    if (blk < nblk_need) {
+      id = blk < kIdsCached ? s_ids[blk] : trow[blk];
+      id = __builtin_amdgcn_readfirstlane(id);
+      if (static_cast<unsigned>(id) < static_cast<unsigned>(p.num_blocks)) {
+        rows = min(kBlock, n - blk * kBlock);
+      } else {
+        bad = 1;
+        id = 0;
       }
-      ts.sc_ok = (tt & 15) < rws;
-      ts.sc = sc_pool + (static_cast<size_t>(ids) * p.num_kv_heads + kh) * kBlock + (tt & 15);
+    }
+    return id;
+  };
+  auto tile_src = [&](int tile, TileSrc& ts) {
+    const int blk0 = tile * (kTile / kBlock) + 2 * th;   // this group's first block of the tile
+    int rk0, rk1;
+    const int id0 = block_src(blk0, rk0);
+    const int id1 = block_src(blk0 + 1, rk1);
+    ts.k[0] = rsrc(kpool + head_off + id0 * blk_stride, rk0 * kRowBytes);
+    ts.k[1] = rsrc(kpool + head_off + id1 * blk_stride, rk1 * kRowBytes);
+    const bool v1 = (wl >> 1) != 0;
+    ts.v = rsrc(vpool + head_off + (v1 ? id1 : id0) * blk_stride, (v1 ? rk1 : rk0) * kRowBytes);
+    if constexpr (kI8) {
+      // scale of token 32 th + (tl % 32): K for tl % 64 < 32, V otherwise
+      const int t = tl & 31;
+      const bool hi = t >= kBlock;
+      ts.sc_ok = (t & 15) < (hi ? rk1 : rk0);
+      ts.sc = sc_pool + (static_cast<size_t>(hi ? id1 : id0) * p.num_kv_heads + kh) * kBlock + (t & 15);
     }
   };
   // The loads themselves: the same 4 (+1 scale) loads for every tile, no branch.
-  const int koff = (tg & 15) * kRowBytes + u16 * kUnit;            // K chunk i: row tg % 16 of block th + 2 i
-  const int voff = ((2 * tg) & 15) * kRowBytes + u16 * kUnit;      // V: rows 2 tg % 16, + 1 of block w / 2
+  const int koff = tg * kRowBytes + u16 * kUnit;                   // K chunk i: row tg of block 2 th + i
+  const int voff = ((2 * tg) & 15) * kRowBytes + u16 * kUnit;      // V: rows 2 tg % 16, + 1
   auto gissue = [&](const TileSrc& ts, Staged& st) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -301,9 +282,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   };
 
   // LDS byte offsets of this thread's stores, the same for every stage
-  const int kw_off = k_off(tg, u16);                 // K chunk i: token tg + 32 i, + 8192 i
-  // V^T: dims 8 u + e, tokens 2 tg, 2 tg + 1 (4 bytes in unit tg / 4)
-  auto vw_off = [&](int e) { return kKBytes + vt_off(8 * u16 + e, tg >> 2) + ((tg & 3) << 2); };
+  const int kw_off = k_off(32 * th + tg, u16);       // K chunk i: token 32 th + tg + 16 i, + 4096 i
+  // V^T: dims 8 u + e, tokens 32 th + 2 tg, + 1 (4 bytes in unit 4 th + tg / 4)
+  auto vw_off = [&](int e) { return kKBytes + vt_off(8 * u16 + e, 4 * th + (tg >> 2)) + ((tg & 3) << 2); };
 
   // K chunk i of st -> bf16 (int8 codes converted)
   auto k_bf16 = [&](const Staged& st, int i) -> uint4 {
@@ -331,21 +312,21 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       }
     }
   };
-  // dim 8 u + e of tokens 2 tg, 2 tg + 1, packed
+  // dim 8 u + e of the two tokens, packed
   auto v_pair = [&](const uint32_t (&vw)[2][4], int e) -> uint32_t {
     return __builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
   };
   auto sc_store = [&](const Staged& st, int stage) {
     if constexpr (kI8) {
-      // threads t, t + 128, t + 256, t + 384 store the same value to the same place
+      // the 4 wavefronts of a group store the same values to the same places
       const float sc = st.sc_ok ? st.sc : 0.f;
-      s_sc[stage][tid & (2 * kTile - 1)] = (tid & kTile) ? sc : sc * p.scale_log2;
+      s_sc[stage][((tl & 32) ? kTile : 0) + 32 * th + (tl & 31)] = (tl & 32) ? sc : sc * p.scale_log2;
     }
   };
   auto lstore = [&](const Staged& st, int stage) {
     char* sb = s_kv[stage];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(sb + kw_off + 8192 * i) = k_bf16(st, i);
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(sb + kw_off + 4096 * i) = k_bf16(st, i);
     uint32_t vw[2][4];
     v_bf16(st, vw);
 #pragma unroll
@@ -382,15 +363,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
   f32x16_t sacc;   // S^T of the tile being softmaxed
+  bf16x8_t phi[2], plo[2];   // P^T of that tile: bf16 high parts and residuals
 
   // scores: register v of the wavefront's half holds token
   // 32 th + 8 h + 16 (v / 8) + (v % 8) of the tile; chunk c = v / 4
   auto tok_of = [&](int v) { return 32 * th + 8 * h + 16 * (v >> 3) + (v & 7); };
 
-  // Phase 1: softmax of tile j (scores in sacc, scales in stage ss) || S^T
-  // of tile j + 1 (K in stage sk) into sn, in 8 slots of one MFMA.
-  auto phase1 = [&](auto diag_tag, int j, int sk, int ss, f32x16_t& sn, bf16x8_t (&phi)[2], bf16x8_t (&plo)[2],
-                    uint4 (&va0)[4], int sv_stage) -> float {
+  // Phase 1 of tile j: the softmax of its scores (sacc, scales in stage ss)
+  // || S^T of tile j + 1 (K in stage sk), in 8 slots of one MFMA; then O is
+  // rescaled if the reference max moved and sacc becomes tile j + 1's S^T.
+  auto phase1 = [&](auto diag_tag, int j, int sk, int ss) {
     constexpr bool kDiag = decltype(diag_tag)::value;
     const char* kb = s_kv[sk];
     const float* scs = s_sc[ss];
@@ -405,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     float sv[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) sv[v] = sacc[v];
-    sn = f32x16_t{};
+    f32x16_t sn = f32x16_t{};
     auto mfma1 = [&](int ks) {
       sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks % 3]), qb[ks], sn, 0, 0, 0);
       if (ks + 3 < 8) ka[ks % 3] = lds_read16(kb + kr_off[ks + 3]);
@@ -435,6 +417,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     }
     // slots 4-7: exponentials of scores 4 c .. 4 c + 3 (the reference max first)
     float corr = 1.f, mu = 0.f, rsum = 0.f;
+    uint32_t pw_hi[8], pw_lo[8];   // P^T words: registers 2 k, 2 k + 1
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       mfma1(4 + c);
@@ -454,41 +437,49 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
         vv[0] = sc4.x; vv[1] = sc4.y; vv[2] = sc4.z; vv[3] = sc4.w;
         if (c < 3) read_sc(kTile + tok_of(4 * (c + 1)));
       }
-      if (c == 3) {
-        // the first k-step's V operands of phase 2
-        const char* vb = s_kv[sv_stage];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) va0[db] = lds_read16(vb + vr_off[db][0]);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 4; e += 2) {
         const int v = 4 * c + e;
-        float pw;
-        if constexpr (kI8) pw = __builtin_amdgcn_exp2f(sv[v] - mu);
-        else pw = __builtin_amdgcn_exp2f(fmaf(sv[v], p.scale_log2, -mu));
-        rsum += pw;
-        if constexpr (kI8) pw *= vv[e];
-        const __bf16 hi = static_cast<__bf16>(pw);
-        phi[v >> 3][v & 7] = hi;
-        plo[v >> 3][v & 7] = static_cast<__bf16>(pw - static_cast<float>(hi));
+        float pw[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          if constexpr (kI8) pw[k] = __builtin_amdgcn_exp2f(sv[v + k] - mu);
+          else pw[k] = __builtin_amdgcn_exp2f(fmaf(sv[v + k], p.scale_log2, -mu));
+          rsum += pw[k];
+          if constexpr (kI8) pw[k] *= vv[e + k];
+        }
+        // high parts rounded to bf16, residuals exact in float32 then rounded
+        const uint32_t hp = pack_bf16(pw[0], pw[1]);
+        const uint32_t lp = pack_bf16(pw[0] - __uint_as_float(hp << 16), pw[1] - __uint_as_float(hp & 0xffff0000u));
+        pw_hi[v >> 1] = hp;
+        pw_lo[v >> 1] = lp;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     rsum += __shfl_xor(rsum, 32);
     l += rsum;
-    return corr;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      phi[k2] = __builtin_bit_cast(bf16x8_t, make_uint4(pw_hi[4 * k2], pw_hi[4 * k2 + 1], pw_hi[4 * k2 + 2], pw_hi[4 * k2 + 3]));
+      plo[k2] = __builtin_bit_cast(bf16x8_t, make_uint4(pw_lo[4 * k2], pw_lo[4 * k2 + 1], pw_lo[4 * k2 + 2], pw_lo[4 * k2 + 3]));
+    }
+    if (wave_any(corr != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= corr;
+    }
+    sacc = sn;   // S^T of tile j + 1 (garbage past the last tile, unused)
   };
 
-  // Phase 2: O^T += V^T P^T over this wavefront's 32 tokens (V in stage
-  // sv_stage) || tile j + 2 from st to stage st_stage, then tile j + 4's
-  // loads into st; 8 slots of two MFMAs on different accumulators.
-  auto phase2 = [&](int sv_stage, int st_stage, const bf16x8_t (&phi)[2], const bf16x8_t (&plo)[2],
-                    uint4 (&va0)[4], Staged& st, const TileSrc& ns) {
+  // Phase 2 of tile j: O^T += V_j^T P_j^T over this wavefront's 32 tokens
+  // (V in stage sv_stage) || this group's half of tile j + 2 from st to
+  // stage st_stage, then tile j + 3's loads (from ns) into st; 8 slots of two
+  // MFMAs on different accumulators.
+  auto phase2 = [&](int j, int sv_stage, int st_stage, Staged& st, const TileSrc& ns) {
     const char* vb = s_kv[sv_stage];
     char* wb = s_kv[st_stage];
     uint4 va[2][4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) va[0][db] = va0[db];
+    for (int db = 0; db < 4; ++db) va[0][db] = lds_read16(vb + vr_off[db][0]);
     uint32_t vw[2][4];
     // slot s: k-step k2 = s / 4; (s % 4) = high part of dims blocks 0,1 / 2,3,
     // then the residual of 0,1 / 2,3
@@ -505,9 +496,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
         const int db = 2 * (q & 1) + d2;
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va[k2][db]), b, o[db], 0, 0, 0);
       }
-      // staging of tile j + 2 (st -> LDS stage st_stage), then tile j + 4's loads
+      // staging of tile j + 2 (st -> LDS stage st_stage), then tile j + 3's loads
       if (sl < 2) {
-        *reinterpret_cast<uint4*>(wb + kw_off + 8192 * sl) = k_bf16(st, sl);
+        *reinterpret_cast<uint4*>(wb + kw_off + 4096 * sl) = k_bf16(st, sl);
       } else if (sl == 2) {
         v_bf16(st, vw);
       } else if (sl < 7) {
@@ -524,52 +515,46 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     }
   };
 
-  // ---- prologue: tiles 0 and 1 in LDS, tiles 2 and 3 in flight, S^T of tile 0 ----
-  Staged sa{}, sb{};
-  gload(0, sa);
-  gload(1, sb);
-  lstore(sa, 0);
-  lstore(sb, 1);
+  // ---- prologue: this group's halves of tiles 0 and 1 in LDS, tile 2 in
+  // flight, S^T of tile 0 ----
+  Staged sa{};
+  {
+    Staged sb{};
+    gload(0, sa);
+    gload(1, sb);
+    lstore(sa, 0);
+    lstore(sb, 1);
+  }
   gload(2, sa);
-  gload(3, sb);
   __syncthreads();
   qk(0, sacc);
 
-  int st0 = 0;   // stage of tile j
-  auto iter = [&](auto diag_tag, int j, Staged& st) {
-    const int st1 = st0 == 2 ? 0 : st0 + 1;
+  // ---- main loop. Every wavefront runs phase 1 and phase 2 of each tile
+  // with a barrier after each; group 1 passes one extra barrier before the
+  // loop and group 0 one after it, so group 1 runs exactly one phase behind:
+  // on each SIMD one group's softmax issues beside the other group's PV
+  // MFMAs. The groups share no staged data; within a group the barriers
+  // order the staging of a tile before its use and the reuse of a stage
+  // after its last read. ----
+  int stj = 0;   // stage of this group's tile j
+  auto iter = [&](auto diag_tag, int j) {
+    const int st1 = stj == 2 ? 0 : stj + 1;
     const int st2 = st1 == 2 ? 0 : st1 + 1;
-    TileSrc nsrc;
-    tile_src(j + 4, nsrc);
-    bf16x8_t phi[2], plo[2];
-    f32x16_t snext;
-    uint4 va0[4];
+    TileSrc ns;
+    tile_src(j + 3, ns);
     __builtin_amdgcn_sched_barrier(0);
-    // S^T of tile j + 1 is garbage past the last tile (unused)
-    const float corr = phase1(diag_tag, j, st1, st0, snext, phi, plo, va0, st0);
-    if (wave_any(corr != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= corr;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // stage st2 receives stale data past the last tile (never read)
-    phase2(st0, st2, phi, plo, va0, st, nsrc);
+    phase1(diag_tag, j, st1, stj);
     __syncthreads();
-    sacc = snext;
-    st0 = st1;
+    phase2(j, stj, st2, sa, ns);
+    stj = st1;
+    __syncthreads();
   };
-  // tiles before the diagonal need no mask; the loops start at even tiles,
-  // so tile j always stages through register set j % 2
-  const int fd2 = min(first_diag, ntiles) & ~1;
+  if (th == 1) __syncthreads();
+  const int fdc = min(first_diag, ntiles);
   int j = 0;
-  for (; j < fd2; j += 2) {
-    iter(std::false_type{}, j, sa);
-    iter(std::false_type{}, j + 1, sb);
-  }
-  for (; j < ntiles; j += 2) {
-    iter(std::true_type{}, j, sa);
-    if (j + 1 < ntiles) iter(std::true_type{}, j + 1, sb);
-  }
+  for (; j < fdc; ++j) iter(std::false_type{}, j);
+  for (; j < ntiles; ++j) iter(std::true_type{}, j);
+  if (th == 0) __syncthreads();
 
   // ---- merge the two token halves: wavefront w + 4 hands (o, m, l) to w ----
   bad = __syncthreads_or(bad);   // also: every wavefront is done with the stages
