@@ -164,6 +164,35 @@ pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t ba
                                       void* stream);
 
 /*
+ * paged_attention_decode_append: pkv_reshape_and_cache of the step's new
+ * rows followed by pkv_paged_attention_decode, in one pass (page
+ * "llm-inference" on shehab-ashraf.github.io, section "KV Cache", subsection
+ * "The Idea": the step's k, v are appended, then its q attends over the whole
+ * history). The wavefront that reads a sequence's last block first writes
+ * that sequence's new K/V rows to their slot, with the same arithmetic as
+ * pkv_reshape_and_cache (int8 codes and scales bit for bit), and waits for the
+ * stores before it reads the block.
+ *   k_new, v_new : [batch][num_kv_heads][head_dim] of src_dtype, 16-byte
+ *                  aligned; one new token per sequence. src_dtype as for
+ *                  pkv_reshape_and_cache.
+ *   slot_mapping : int64 [batch]; slot of sequence b's new token, which must
+ *                  be the slot of its position n_b - 1 in its block table
+ *                  (otherwise the result is unspecified). Slots outside the
+ *                  pool are skipped.
+ *   the rest     : as pkv_paged_attention_decode, split mode only:
+ *                  max_num_splits == 0 returns PKV_ERR_UNSUPPORTED.
+ * Sequences whose split count is invalid (their outputs are NaN) may be
+ * left without their new rows written.
+ */
+pkv_status pkv_paged_attention_decode_append(const void* k_new, const void* v_new, int32_t src_dtype,
+                                             const int64_t* slot_mapping, const void* q, int32_t q_dtype,
+                                             int32_t batch, int32_t num_q_heads, const pkv_cache* cache,
+                                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                             const int32_t* context_lens, const int32_t* num_splits,
+                                             int32_t max_num_splits, float scale, float* out, float* out_lse,
+                                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_attention_chunked: causal query chunks against their cached prefix
  * (chunked prefill, course README curriculum S11; the chunk's own K/V must
  * already be in the cache, written by pkv_reshape_and_cache).

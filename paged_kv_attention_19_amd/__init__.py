@@ -8,8 +8,9 @@ current HIP stream to the C entry points. There is no CPU fallback: if the
 library is missing, or the tensors are not on a GPU, the calls raise.
 
 Names follow the C ABI: :func:`reshape_and_cache`,
-:func:`paged_attention_decode`, :func:`paged_attention_chunked`,
-:func:`lse_combine`, :func:`decode_workspace_bytes`.
+:func:`paged_attention_decode`, :func:`paged_attention_decode_append`,
+:func:`paged_attention_chunked`, :func:`lse_combine`,
+:func:`decode_workspace_bytes`.
 """
 
 from __future__ import annotations
@@ -24,7 +25,7 @@ import torch
 __all__ = [
     "F32", "BF16", "I8", "PkvError", "KVCache", "lib", "library_path", "exported_symbols",
     "reshape_and_cache", "decode_workspace_bytes", "paged_attention_decode",
-    "paged_attention_chunked", "lse_combine", "version",
+    "paged_attention_decode_append", "paged_attention_chunked", "lse_combine", "version",
 ]
 
 F32, BF16, I8 = 0, 1, 2
@@ -69,6 +70,8 @@ _SIGS = {
     "pkv_decode_workspace_bytes": ([_I32, _I32, _I32, _I32], ctypes.c_size_t),
     "pkv_paged_attention_decode": ([_P, _I32, _I32, _I32, ctypes.POINTER(_Cache), _P, _I32, _P, _P, _I32,
                                     ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], _I32),
+    "pkv_paged_attention_decode_append": ([_P, _P, _I32, _P, _P, _I32, _I32, _I32, ctypes.POINTER(_Cache), _P, _I32,
+                                           _P, _P, _I32, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], _I32),
     "pkv_paged_attention_chunked": ([_P, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Cache), _P, _I32, _P,
                                      ctypes.c_float, _P, _P, _P], _I32),
     "pkv_lse_combine": ([_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
@@ -273,6 +276,56 @@ def paged_attention_decode(q: torch.Tensor, cache: KVCache, block_tables: torch.
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     d = cache.descriptor()
     _check(lib().pkv_paged_attention_decode(
+        q.data_ptr(), _CODE[q.dtype], B, Hq, ctypes.byref(d), block_tables.data_ptr(), block_tables.shape[1],
+        context_lens.data_ptr(), _ptr(num_splits), max_num_splits, float(scale), out.data_ptr(),
+        _ptr(out_lse), _ptr(workspace), ws_bytes, _stream_handle()))
+    return (out, out_lse) if (return_lse or out_lse is not None) else out
+
+
+def paged_attention_decode_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                                  q: torch.Tensor, cache: KVCache, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, num_splits: torch.Tensor | None,
+                                  max_num_splits: int, scale: float, out: torch.Tensor | None = None,
+                                  out_lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                                  return_lse: bool = False):
+    """:func:`reshape_and_cache` of the step's new rows ``[B][Hkv][D]`` (one per
+    sequence, at ``slot_mapping``) followed by :func:`paged_attention_decode`,
+    in one pass. Split mode only (``max_num_splits >= 1``)."""
+    _need(q, "q", (torch.float32, torch.bfloat16), 3)
+    B, Hq, D = q.shape
+    _need(k_new, "k_new", (torch.float32, torch.bfloat16), 3)
+    _need(v_new, "v_new", (k_new.dtype,), 3)
+    _need(slot_mapping, "slot_mapping", (torch.int64,), 1)
+    if tuple(k_new.shape) != (B, cache.num_kv_heads, cache.head_dim) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError(f"new rows are {tuple(k_new.shape)}, want ({B}, {cache.num_kv_heads}, {cache.head_dim})")
+    if slot_mapping.shape[0] != B:
+        raise ValueError("slot_mapping batch mismatch")
+    _need(block_tables, "block_tables", (torch.int32,), 2)
+    _need(context_lens, "context_lens", (torch.int32,), 1)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens batch mismatch")
+    if D != cache.head_dim:
+        raise ValueError(f"q head_dim {D} != cache head_dim {cache.head_dim}")
+    if num_splits is not None:
+        _need(num_splits, "num_splits", (torch.int32,), 1)
+        if num_splits.shape[0] != B:
+            raise ValueError("num_splits batch mismatch")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out shape")
+    if out_lse is None and return_lse:
+        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if out_lse is not None:
+        _need(out_lse, "out_lse", (torch.float32,), 2)
+    need = decode_workspace_bytes(B, Hq, D, max_num_splits) if max_num_splits > 0 else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = cache.descriptor()
+    _check(lib().pkv_paged_attention_decode_append(
+        k_new.data_ptr(), v_new.data_ptr(), _CODE[k_new.dtype], slot_mapping.data_ptr(),
         q.data_ptr(), _CODE[q.dtype], B, Hq, ctypes.byref(d), block_tables.data_ptr(), block_tables.shape[1],
         context_lens.data_ptr(), _ptr(num_splits), max_num_splits, float(scale), out.data_ptr(),
         _ptr(out_lse), _ptr(workspace), ws_bytes, _stream_handle()))

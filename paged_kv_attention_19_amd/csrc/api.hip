@@ -177,16 +177,20 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t he
   return (bytes + 255) & ~static_cast<size_t>(255);
 }
 
-pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
-                                      const pkv_cache* cache, const int32_t* block_tables,
-                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                      const int32_t* num_splits, int32_t max_num_splits, float scale, float* out,
-                                      float* out_lse, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "pkv_paged_attention_decode";
+// Argument checks shared by the decode entry points; *empty is set when there
+// is nothing to launch (batch == 0).
+static pkv_status check_decode(const char* fn, const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                               const pkv_cache* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, const int32_t* num_splits, int32_t max_num_splits,
+                               float scale, const float* out, const void* workspace, size_t workspace_bytes,
+                               bool* empty) {
   if (pkv_status st = check_cache(cache, fn); st != PKV_OK) return st;
   if (batch < 0) return fail(PKV_ERR_INVALID_ARG, "%s: batch=%d", fn, batch);
   if (pkv_status st = check_group(num_q_heads, cache->num_kv_heads, fn); st != PKV_OK) return st;
-  if (batch == 0) return ok();
+  if (batch == 0) {
+    *empty = true;
+    return ok();
+  }
   if (batch > 65535) return fail(PKV_ERR_UNSUPPORTED, "%s: batch=%d (built: <= 65535)", fn, batch);
   if (q_dtype != PKV_F32 && q_dtype != PKV_BF16)
     return fail(PKV_ERR_INVALID_ARG, "%s: q_dtype=%s (F32 or BF16)", fn, dtype_name(q_dtype));
@@ -213,7 +217,101 @@ pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t ba
     return fail(PKV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace == nullptr ? size_t(0) : workspace_bytes);
   if (need > 0 && !aligned16(workspace)) return fail(PKV_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
+  return ok();
 
+}
+
+// Split mode (max_num_splits >= 1): the partial pass, then the merge when
+// there are several splits and an output. `append` (may be null) adds the
+// step's new rows to the pass. The arguments have been checked.
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  int32_t src_dtype;
+  const int64_t* slots;
+};
+
+static pkv_status run_split_decode(const char* fn, const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                   const pkv_cache* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, const int32_t* num_splits, int32_t max_num_splits,
+                                   float scale, float* out, float* out_lse, void* workspace,
+                                   const AppendArgs* append, void* stream) {
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int D = cache->head_dim;
+  const int group = num_q_heads / cache->num_kv_heads;
+  const bool direct = max_num_splits == 1;
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = direct ? nullptr : o_part + static_cast<size_t>(batch) * max_num_splits * num_q_heads * D;
+
+  pkv::DecodeParams p{};
+  p.q = q;
+  p.k = cache->k;
+  p.v = cache->v;
+  p.k_scale = cache->k_scale;
+  p.v_scale = cache->v_scale;
+  p.tables = block_tables;
+  p.ctx = context_lens;
+  p.nsplits = num_splits;
+  p.o = direct ? out : o_part;
+  p.lse = direct ? out_lse : lse_part;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_blocks = cache->num_blocks;
+  p.max_ns = max_num_splits;
+  p.direct = direct ? 1 : 0;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.batch = batch;
+  if (append != nullptr) {
+    p.k_new = append->k_new;
+    p.v_new = append->v_new;
+    p.slots = append->slots;
+    p.new_dtype = append->src_dtype;
+    p.k_w = cache->k;
+    p.v_w = cache->v;
+    p.k_scale_w = cache->k_scale;
+    p.v_scale_w = cache->v_scale;
+    p.num_slots = static_cast<int64_t>(cache->num_blocks) * cache->block_size;
+  }
+  const int waves = decode_waves(max_blocks_per_seq, max_num_splits);
+  const bool deep = decode_deep(batch, max_num_splits, cache->num_kv_heads, waves);
+  hipError_t e;
+  switch (cache->kv_dtype) {
+    case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, waves, deep, st); break;
+    case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, waves, deep, st); break;
+    default: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, waves, deep, st); break;
+  }
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (!direct && out != nullptr) {
+    pkv::CombineParams cp{};
+    cp.o_part = o_part;
+    cp.lse_part = lse_part;
+    cp.nsplits = num_splits;
+    cp.out = out;
+    cp.out_lse = out_lse;
+    cp.batch = batch;
+    cp.num_q_heads = num_q_heads;
+    cp.max_ns = max_num_splits;
+    e = pkv::launch_combine(cp, D, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+  }
+  return ok();
+}
+
+pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                      const pkv_cache* cache, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                      const int32_t* num_splits, int32_t max_num_splits, float scale, float* out,
+                                      float* out_lse, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "pkv_paged_attention_decode";
+  bool empty = false;
+  if (pkv_status st = check_decode(fn, q, q_dtype, batch, num_q_heads, cache, block_tables, max_blocks_per_seq,
+                                   context_lens, num_splits, max_num_splits, scale, out, workspace, workspace_bytes,
+                                   &empty);
+      st != PKV_OK || empty)
+    return st;
+  const bool balanced = max_num_splits == 0;
+  const int D = cache->head_dim;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int group = num_q_heads / cache->num_kv_heads;
   if (balanced) {
@@ -248,52 +346,42 @@ pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t ba
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
   }
-  const bool direct = max_num_splits == 1;
-  float* o_part = static_cast<float*>(workspace);
-  float* lse_part = direct ? nullptr : o_part + static_cast<size_t>(batch) * max_num_splits * num_q_heads * D;
+  return run_split_decode(fn, q, q_dtype, batch, num_q_heads, cache, block_tables, max_blocks_per_seq, context_lens,
+                          num_splits, max_num_splits, scale, out, out_lse, workspace, nullptr, stream);
+}
 
-  pkv::DecodeParams p{};
-  p.q = q;
-  p.k = cache->k;
-  p.v = cache->v;
-  p.k_scale = cache->k_scale;
-  p.v_scale = cache->v_scale;
-  p.tables = block_tables;
-  p.ctx = context_lens;
-  p.nsplits = num_splits;
-  p.o = direct ? out : o_part;
-  p.lse = direct ? out_lse : lse_part;
-  p.num_q_heads = num_q_heads;
-  p.num_kv_heads = cache->num_kv_heads;
-  p.max_blocks = max_blocks_per_seq;
-  p.num_blocks = cache->num_blocks;
-  p.max_ns = max_num_splits;
-  p.direct = direct ? 1 : 0;
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.batch = batch;
-  const int waves = decode_waves(max_blocks_per_seq, max_num_splits);
-  const bool deep = decode_deep(batch, max_num_splits, cache->num_kv_heads, waves);
-  hipError_t e;
-  switch (cache->kv_dtype) {
-    case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, waves, deep, st); break;
-    case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, waves, deep, st); break;
-    default: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, waves, deep, st); break;
+pkv_status pkv_paged_attention_decode_append(const void* k_new, const void* v_new, int32_t src_dtype,
+                                             const int64_t* slot_mapping, const void* q, int32_t q_dtype,
+                                             int32_t batch, int32_t num_q_heads, const pkv_cache* cache,
+                                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                             const int32_t* context_lens, const int32_t* num_splits,
+                                             int32_t max_num_splits, float scale, float* out, float* out_lse,
+                                             void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "pkv_paged_attention_decode_append";
+  if (max_num_splits == 0)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: the balanced mode (max_num_splits = 0) has no append", fn);
+  bool empty = false;
+  if (pkv_status st = check_decode(fn, q, q_dtype, batch, num_q_heads, cache, block_tables, max_blocks_per_seq,
+                                   context_lens, num_splits, max_num_splits, scale, out, workspace, workspace_bytes,
+                                   &empty);
+      st != PKV_OK || empty)
+    return st;
+  if (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "%s: k_new/v_new/slot_mapping is NULL", fn);
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(PKV_ERR_INVALID_ARG, "%s: k_new/v_new not 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: slot_mapping not 8-byte aligned", fn);
+  const int kv = cache->kv_dtype;
+  if (kv == PKV_I8) {
+    if (src_dtype != PKV_F32 && src_dtype != PKV_BF16)
+      return fail(PKV_ERR_INVALID_ARG, "%s: I8 cache takes F32 or BF16 rows, got %s", fn, dtype_name(src_dtype));
+  } else if (src_dtype != kv) {
+    return fail(PKV_ERR_INVALID_ARG, "%s: %s cache needs %s rows, got %s", fn, dtype_name(kv), dtype_name(kv),
+                dtype_name(src_dtype));
   }
-  if (e != hipSuccess) return hip_fail(e, fn);
-  if (!direct && out != nullptr) {
-    pkv::CombineParams cp{};
-    cp.o_part = o_part;
-    cp.lse_part = lse_part;
-    cp.nsplits = num_splits;
-    cp.out = out;
-    cp.out_lse = out_lse;
-    cp.batch = batch;
-    cp.num_q_heads = num_q_heads;
-    cp.max_ns = max_num_splits;
-    e = pkv::launch_combine(cp, D, st);
-    if (e != hipSuccess) return hip_fail(e, fn);
-  }
-  return ok();
+  const AppendArgs append{k_new, v_new, src_dtype, slot_mapping};
+  return run_split_decode(fn, q, q_dtype, batch, num_q_heads, cache, block_tables, max_blocks_per_seq, context_lens,
+                          num_splits, max_num_splits, scale, out, out_lse, workspace, &append, stream);
 }
 
 pkv_status pkv_lse_combine(const float* o_part, const float* lse_part, int32_t batch, int32_t num_q_heads,

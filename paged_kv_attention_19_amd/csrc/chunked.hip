@@ -575,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   const float a1 = (m == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(m - mm);
   const float a2 = (m2 == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
   const float lt = l * a1 + l2 * a2;
-  const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+  const float inv = norm_inv(lt);
 
   // ---- write: lane holds dims 32 db + 8 (v / 4) + 4 h + v % 4 of its row ----
 #pragma unroll
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     }
   }
   if (h == 0 && p.lse != nullptr) {
-    const float lse = bad ? qnan() : (lt > 0.f ? (mm + log2f(lt)) * kLn2 : neg_inf());
+    const float lse = bad ? qnan() : norm_lse2(mm, lt);
     p.lse[static_cast<size_t>(q0 + pi) * p.num_q_heads + hq] = lse;
   }
 }

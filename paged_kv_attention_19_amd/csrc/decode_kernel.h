@@ -23,8 +23,44 @@
 #pragma once
 
 #include "decode_core.h"
+#include "quant_row.h"
 
 namespace pkv {
+
+// Append (split mode): the whole wavefront writes the new K and V rows of kv
+// head kh of sequence b to slot p.slots[b] (skipped when the slot is outside
+// the pool), with the same per-row arithmetic as reshape_and_cache.
+template <int SRC, int D>
+__device__ __forceinline__ void append_quant(const DecodeParams& p, int64_t row, int64_t dst_row, int lane) {
+  constexpr int R = D / KvGeom<SRC>::kEpl;   // lanes per row: K on lanes [0, R), V on [R, 2R)
+  if (lane < 2 * R) {
+    const bool isv = lane >= R;
+    quantize_row_piece<SRC, D>(isv ? p.v_new : p.k_new, isv ? p.v_w : p.k_w, isv ? p.v_scale_w : p.k_scale_w, row,
+                               dst_row, lane % R);
+  }
+}
+
+template <int KV, int D>
+__device__ __forceinline__ void append_rows(const DecodeParams& p, int b, int kh, int lane) {
+  const int64_t slot = p.slots[b];
+  if (slot < 0 || slot >= p.num_slots) return;
+  const int64_t row = static_cast<int64_t>(b) * p.num_kv_heads + kh;
+  const int64_t dst_row = ((slot / kBlock) * p.num_kv_heads + kh) * kBlock + slot % kBlock;
+  if constexpr (KV == PKV_I8) {
+    if (p.new_dtype == PKV_BF16) append_quant<PKV_BF16, D>(p, row, dst_row, lane);
+    else append_quant<PKV_F32, D>(p, row, dst_row, lane);
+  } else {
+    constexpr int kRowBytes = D * KvGeom<KV>::kEsize;
+    constexpr int kPieces = kRowBytes / 16;
+    for (int i = lane; i < 2 * kPieces; i += kWave) {   // K pieces, then V pieces
+      const bool isv = i >= kPieces;
+      const int piece = isv ? i - kPieces : i;
+      const char* src = static_cast<const char*>(isv ? p.v_new : p.k_new) + row * kRowBytes + piece * 16;
+      char* dst = static_cast<char*>(isv ? p.v_w : p.k_w) + dst_row * kRowBytes + piece * 16;
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    }
+  }
+}
 
 template <int KV, int QT, int D, int G, int NW, int PD>
 __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p) {
@@ -72,10 +108,10 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
   if (ns < 1 || s >= ns) return;  // not a split of this sequence (the merge checks ns)
 
   const bool bad_n = (n < 0) || (static_cast<int64_t>(n) > static_cast<int64_t>(p.max_blocks) * kBlock);
-  int t0 = 0, t1 = 0;
+  int t0 = 0, t1 = 0, tps = 0;
   if (!bad_n && n > 0) {
     const int per = (n + ns - 1) / ns;
-    const int tps = ((per + kBlock - 1) / kBlock) * kBlock;
+    tps = ((per + kBlock - 1) / kBlock) * kBlock;
     const int64_t a = static_cast<int64_t>(s) * tps;
     t0 = a < n ? static_cast<int>(a) : n;
     t1 = (static_cast<int64_t>(t0) + tps) < n ? t0 + tps : n;
@@ -83,6 +119,22 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
   const int blk_lo = t0 / kBlock;
   const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
   const int nb_w = nblk > w ? (nblk - w + NW - 1) / NW : 0;
+
+  // Append: the wavefront that reads the block of token n - 1 (in split
+  // (n - 1) / tps, where the block is dealt to wavefront (its index in the
+  // split) % NW; trailing splits may be empty) writes the new rows first and
+  // waits for those stores to complete before it issues any load, so its read
+  // of the block sees them. No other wavefront reads that block. With no
+  // tokens to read, split 0's wavefront 0 writes them.
+  if (p.k_new != nullptr) {
+    const bool has_tail = !bad_n && n > 0;
+    const int s_tail = has_tail ? (n - 1) / tps : 0;
+    const int w_tail = has_tail ? ((n - 1) / kBlock - blk_lo) % NW : 0;
+    if (s == s_tail && w == w_tail) {
+      append_rows<KV, D>(p, b, kh, lane);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    }
+  }
 
   wd.reset();
 
@@ -202,9 +254,12 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
     } else if (L > 0.f) {
       o = O / L;
       lse = (Mx + log2f(L)) * kLn2;
-    } else {
+    } else if (L == 0.f) {
       o = 0.f;
       lse = neg_inf();
+    } else {   // a NaN was read
+      o = qnan();
+      lse = qnan();
     }
     const int h = h0 + g;
     const size_t row = p.direct ? static_cast<size_t>(b) * p.num_q_heads + h
@@ -371,7 +426,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float L = wd.l[g];
-          const float inv = L > 0.f ? 1.f / L : 0.f;
+          const float inv = norm_inv(L);
           float* out = p.o + (static_cast<size_t>(sb) * Hq + h0 + g) * D;
 #pragma unroll
           for (int j = 0; j < CPL; ++j) {
@@ -380,7 +435,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
           }
           if (lane == 0 && p.lse != nullptr)
             p.lse[static_cast<size_t>(sb) * Hq + h0 + g] =
-                sbad ? qnan() : (L > 0.f ? (M[g] + log2f(L)) * kLn2 : neg_inf());
+                sbad ? qnan() : norm_lse2(M[g], L);
         }
       }
     } else {
@@ -396,7 +451,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float L = wd.l[g];
-          const float inv = L > 0.f ? 1.f / L : 0.f;
+          const float inv = norm_inv(L);
 #pragma unroll
           for (int j = 0; j < CPL; ++j) {
 #pragma unroll
@@ -405,7 +460,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
           if (lane == 0)
-            __hip_atomic_store(part + G * D + g, sbad ? qnan() : (L > 0.f ? (M[g] + log2f(L)) * kLn2 : neg_inf()),
+            __hip_atomic_store(part + G * D + g, sbad ? qnan() : norm_lse2(M[g], L),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
@@ -477,10 +532,10 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
           const int gk = idx / D;
           const float L = __shfl(Lh, gk);
           const float M = __shfl(mx, gk);
-          const float o = nan ? qnan() : (L > 0.f ? O[k] / L : 0.f);
+          const float o = nan ? qnan() : (L > 0.f ? O[k] / L : (L == 0.f ? 0.f : qnan()));
           p.o[(static_cast<size_t>(sb) * Hq + h0) * D + idx] = o;
           if (idx % D == 0 && p.lse != nullptr)
-            p.lse[static_cast<size_t>(sb) * Hq + h0 + gk] = nan ? qnan() : (L > 0.f ? M + logf(L) : neg_inf());
+            p.lse[static_cast<size_t>(sb) * Hq + h0 + gk] = nan ? qnan() : (L > 0.f ? M + logf(L) : (L == 0.f ? neg_inf() : qnan()));
         }
         if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
       }

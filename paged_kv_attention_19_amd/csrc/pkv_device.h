@@ -109,4 +109,12 @@ __device__ __forceinline__ int readlane(int x, int lane) { return __builtin_amdg
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 __device__ __forceinline__ float qnan() { return __builtin_nanf(""); }
 
+// Normalising an online-softmax state (numerator O, denominator L, base-2
+// reference max M): L > 0 gives O / L and lse = (M + log2 L) ln 2; L == 0 (no
+// key) gives 0 and -inf; a NaN L (a NaN was read) gives NaN.
+__device__ __forceinline__ float norm_inv(float L) { return L > 0.f ? 1.f / L : (L == 0.f ? 0.f : qnan()); }
+__device__ __forceinline__ float norm_lse2(float M, float L) {
+  return L > 0.f ? (M + log2f(L)) * kLn2 : (L == 0.f ? neg_inf() : qnan());
+}
+
 }  // namespace pkv

@@ -43,6 +43,17 @@ struct DecodeParams {
   float scale_log2;        // softmax scale * log2(e)
   float* part;             // balanced mode: partials of cut segments
   int32_t* counters;       // balanced mode: one arrival counter per (sequence, kv head), zero between calls
+  // split mode with append: the step's new rows, written to their slots
+  // before the sequence's last block is read (k_new == nullptr: no append)
+  const void* k_new;       // [batch][num_kv_heads][head_dim] in new_dtype
+  const void* v_new;
+  const int64_t* slots;    // [batch]
+  void* k_w;               // the cache, writable
+  void* v_w;
+  float* k_scale_w;
+  float* v_scale_w;
+  int64_t num_slots;
+  int32_t new_dtype;
 };
 
 struct CombineParams {

@@ -6,15 +6,11 @@
 // K and the same piece of V; consecutive threads cover a row, so both the read
 // of the new rows and the write of each destination row are coalesced.
 //
-// Int8 cache (course README "Build an LLM Inference Engine From Scratch",
-// curriculum S08, symmetric reading of its q = round(w / scale) + zero with
-// zero = 0): a group of R lanes holds one (token, head) row; the group takes
-// amax = max |x|, scale = amax / 127 (IEEE float32 division; amax == 0 gives
-// 1) and code = clamp(rint(x / scale), -127, 127), again with an IEEE
-// division and round-half-to-even, so codes are exactly those of a float32
-// reference.
+// Int8 cache: a group of D / EPL lanes quantizes one (token, head) row (the
+// shared row quantizer of quant_row.h).
 #include "pkv_device.h"
 #include "pkv_launch.h"
+#include "quant_row.h"
 
 namespace pkv {
 
@@ -41,39 +37,6 @@ __global__ __launch_bounds__(256) void reshape_copy_kernel(ReshapeParams p) {
       *reinterpret_cast<const uint4*>(static_cast<const char*>(p.k_new) + src);
   *reinterpret_cast<uint4*>(static_cast<char*>(p.v) + dst) =
       *reinterpret_cast<const uint4*>(static_cast<const char*>(p.v_new) + src);
-}
-
-template <int SRC, int D>
-__device__ __forceinline__ void quantize_row_piece(const void* src_rows, void* codes_out, float* scales_out,
-                                                   int64_t row, int64_t dst_row, int r) {
-  constexpr int EPL = KvGeom<SRC>::kEpl;  // source elements per lane (4 or 8)
-  constexpr int R = D / EPL;              // lanes per row
-  const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const char*>(src_rows) +
-                                                    (row * D + r * EPL) * KvGeom<SRC>::kEsize);
-  float x[EPL];
-  unpack16<SRC>(raw, x);
-  float amax = 0.f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
-  amax = group_max<R>(amax);
-  const float scale = amax > 0.f ? amax / 127.0f : 1.0f;
-  uint32_t packed[EPL / 4];
-#pragma unroll
-  for (int e = 0; e < EPL / 4; ++e) packed[e] = 0;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    float qv = __builtin_rintf(x[e] / scale);
-    qv = fminf(fmaxf(qv, -127.0f), 127.0f);
-    const uint32_t byte = static_cast<uint32_t>(static_cast<int32_t>(qv)) & 0xffu;
-    packed[e / 4] |= byte << (8 * (e % 4));
-  }
-  char* dst = static_cast<char*>(codes_out) + dst_row * D + r * EPL;
-  if constexpr (EPL == 8) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
-  } else {
-    *reinterpret_cast<uint32_t*>(dst) = packed[0];
-  }
-  if (r == 0) scales_out[dst_row] = scale;
 }
 
 template <int SRC, int D>

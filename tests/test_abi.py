@@ -25,8 +25,9 @@ def cache(**kw):
 def test_library_exports_every_header_function():
     L = pkv.lib()
     names = pkv.exported_symbols()
-    assert {"pkv_reshape_and_cache", "pkv_paged_attention_decode", "pkv_paged_attention_chunked",
-            "pkv_lse_combine", "pkv_decode_workspace_bytes", "pkv_last_error", "pkv_version"} <= set(names)
+    assert {"pkv_reshape_and_cache", "pkv_paged_attention_decode", "pkv_paged_attention_decode_append",
+            "pkv_paged_attention_chunked", "pkv_lse_combine", "pkv_decode_workspace_bytes", "pkv_last_error",
+            "pkv_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert "gfx950" in pkv.version()
@@ -85,6 +86,33 @@ def test_reshape_rejects_bad_arguments():
     assert L.pkv_reshape_and_cache(FAKE, FAKE, pkv.I8, FAKE, 4, ctypes.byref(ci8), None) == -1
     assert L.pkv_reshape_and_cache(FAKE, FAKE, pkv.BF16, FAKE, 0, ctypes.byref(c), None) == 0  # nothing to do
     assert L.pkv_reshape_and_cache(FAKE, FAKE, pkv.BF16, FAKE, 4, None, None) == -1
+
+
+def test_decode_append_rejects_bad_arguments():
+    """Every call fails a host check (or has nothing to do), so none launches."""
+    L = pkv.lib()
+
+    def app(c=None, **kw):
+        a = dict(kn=FAKE, vn=FAKE, src=pkv.BF16, slots=FAKE, q=FAKE, q_dtype=pkv.BF16, batch=3, hq=4, maxb=4,
+                 max_ns=1, out=FAKE)
+        a.update(kw)
+        c = c or cache()
+        return L.pkv_paged_attention_decode_append(a["kn"], a["vn"], a["src"], a["slots"], a["q"], a["q_dtype"],
+                                                   a["batch"], a["hq"], ctypes.byref(c), FAKE, a["maxb"], FAKE, None,
+                                                   a["max_ns"], 0.125, a["out"], None, None, 0, None)
+
+    assert app(max_ns=0) == -2               # the balanced mode has no append
+    assert app(kn=None) == -1
+    assert app(vn=None) == -1
+    assert app(slots=None) == -1
+    assert app(src=pkv.F32) == -1            # a bf16 cache takes bf16 rows
+    assert app(c=cache(kv_dtype=pkv.I8, k_scale=FAKE, v_scale=FAKE), src=pkv.I8) == -1
+    assert app(slots=FAKE + 4) == -1         # slot_mapping not 8-byte aligned
+    assert app(kn=FAKE + 8) == -1            # rows not 16-byte aligned
+    assert app(q=None) == -1                 # the decode checks apply too
+    assert app(max_ns=2) == -1               # num_splits NULL with max_num_splits > 1
+    assert pkv.lib().pkv_last_error().decode().startswith("pkv_paged_attention_decode_append")
+    assert app(batch=0) == 0                 # nothing to do
 
 
 def test_chunked_and_combine_reject_bad_arguments():
