@@ -37,7 +37,8 @@ METRIC = "paged-attn decode KV GB/s (% HBM peak) + seq-steps/s; chunked-prefill 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 KERNEL_FILES = ("paged_kv_attention_19_amd/csrc/decode_kernel.h", "paged_kv_attention_19_amd/csrc/decode_core.h",
-                "paged_kv_attention_19_amd/csrc/decode_bf16.hip", "paged_kv_attention_19_amd/csrc/pkv_device.h")
+                "paged_kv_attention_19_amd/csrc/decode_bf16.hip", "paged_kv_attention_19_amd/csrc/pkv_device.h",
+                "paged_kv_attention_19_amd/csrc/quant_row.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_qwen3_traffic.json")
 
 
@@ -99,6 +100,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunked", action="store_true", help="skip the chunked-prefill MFMA measurement")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="write the new rows with a separate reshape_and_cache launch instead of inside the decode")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--workload", default="qwen3_decode", choices=sorted(WORKLOADS),
                     help="the step's shape (default: the Qwen3-0.6B decode step)")
@@ -142,7 +145,7 @@ def copy_reference(nbytes: int):
 class Replica:
     """One independent copy of the workload, resident on the GPU."""
 
-    def __init__(self, step, dev, max_tokens_per_split, balanced=False):
+    def __init__(self, step, dev, max_tokens_per_split, balanced=False, fuse=True):
         import numpy as np
         import torch
 
@@ -184,6 +187,11 @@ class Replica:
         eb, sb = {"f32": (4, 0), "bf16": (2, 0), "i8": (1, 4)}[step.kv_dtype]
         self.kv_bytes = self.tokens * kv_bytes_per_token(step.num_kv_heads, step.head_dim, eb, sb)
         self.batch = B
+        # one pass writes the new rows too (split mode, one split per sequence)
+        self.fused = fuse and not balanced and self.max_ns == 1
+        src_eb = {"f32": 4, "bf16": 2}[step.src_dtype]
+        self.append_bytes = B * (kv_bytes_per_token(step.num_kv_heads, step.head_dim, src_eb)
+                                 + kv_bytes_per_token(step.num_kv_heads, step.head_dim, eb, sb))
 
     def reshape(self):
         import paged_kv_attention_19_amd as pkv
@@ -194,9 +202,17 @@ class Replica:
         pkv.paged_attention_decode(self.q, self.cache, self.tables, self.ctx, self.ns, self.max_ns,
                                    float(self.step.scale), out=self.out, out_lse=self.lse, workspace=self.ws)
 
+    def decode_append(self):
+        import paged_kv_attention_19_amd as pkv
+        pkv.paged_attention_decode_append(self.new_k, self.new_v, self.new_slots, self.q, self.cache, self.tables,
+                                          self.ctx, self.ns, self.max_ns, float(self.step.scale), out=self.out,
+                                          out_lse=self.lse, workspace=self.ws)
+
     def partials(self):
         import paged_kv_attention_19_amd as pkv
-        if self.max_ns <= 1:
+        if self.fused:
+            self.decode_append()
+        elif self.max_ns <= 1:
             self.decode()
         else:
             pkv.paged_attention_decode(self.q, self.cache, self.tables, self.ctx, self.ns, self.max_ns,
@@ -209,8 +225,11 @@ class Replica:
         pkv.lse_combine(self.o_part, self.lse_part, self.ns, out=self.out, out_lse=self.lse)
 
     def step_once(self):
-        self.reshape()
-        self.decode()
+        if self.fused:
+            self.decode_append()
+        else:
+            self.reshape()
+            self.decode()
 
 
 def time_graphs(fn_per_step, reps, steps, steps_per_graph, warmup):
@@ -394,7 +413,8 @@ def main():
     reps = []
     for r in range(args.replicas):
         step = build(W, seed0, args.max_tokens_per_split, args.batch, r)
-        reps.append(Replica(step, dev, args.max_tokens_per_split, balanced=args.decode_mode == "balanced"))
+        reps.append(Replica(step, dev, args.max_tokens_per_split, balanced=args.decode_mode == "balanced",
+                            fuse=not args.no_fuse))
     torch.cuda.synchronize()
     log(f"built {len(reps)} replicas in {time.time() - t0:.1f}s; max_ns={[r.max_ns for r in reps][:4]}...")
 
@@ -423,7 +443,8 @@ def main():
     per_kernel = {}
     n_k = min(steps, 4096)
     sec_p = time_graphs(lambda r: r.partials(), reps, n_k, args.steps_per_graph, 64)
-    dom = "decode_balanced" if reps[0].balanced else "decode_partial"
+    fused = reps[0].fused
+    dom = "decode_balanced" if reps[0].balanced else ("decode_append" if fused else "decode_partial")
     per_kernel[dom] = sec_p / n_k
     if reps[0].max_ns > 1:
         sec_c = time_graphs(lambda r: r.combine(), reps, n_k, args.steps_per_graph, 64)
@@ -431,14 +452,17 @@ def main():
     sec_r = time_graphs(lambda r: r.reshape(), reps, n_k, args.steps_per_graph, 64)
     per_kernel["reshape_and_cache"] = sec_r / n_k
     partial_bytes = sum(reps[i % R].kv_bytes for i in range(n_k)) / n_k
-    achieved = partial_bytes / per_kernel[dom] / 1e9
+    # algorithmic bytes of the dominant launch: the KV it reads, plus, when it
+    # appends, the new rows it reads and writes
+    launch_bytes = partial_bytes + (sum(reps[i % R].append_bytes for i in range(n_k)) / n_k if fused else 0)
+    achieved = launch_bytes / per_kernel[dom] / 1e9
 
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if (tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == args.workload
-                and tr.get("decode_mode") == args.decode_mode
+                and tr.get("decode_mode") == args.decode_mode and tr.get("append") == fused
                 and tr.get("max_tokens_per_split") == args.max_tokens_per_split):
             traffic = tr.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
@@ -461,6 +485,7 @@ def main():
             "batch": reps[0].batch,
             "num_q_heads": 16, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
             "decode_mode": args.decode_mode,
+            "append": "in the decode pass" if fused else "separate reshape_and_cache launch",
             "max_tokens_per_split": None if reps[0].balanced else args.max_tokens_per_split,
             "replicas": R, "kv_bytes_per_step": int(kv_total / steps),
             "parallelism": "none",
@@ -471,6 +496,7 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": "decode_balanced_kernel" if reps[0].balanced else "decode_partial_kernel",
+            "algorithmic_bytes": int(launch_bytes),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
