@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 KERNEL_FILES = ("paged_kv_attention_19_amd/csrc/decode_kernel.h", "paged_kv_attention_19_amd/csrc/decode_core.h",
                 "paged_kv_attention_19_amd/csrc/decode_bf16.hip", "paged_kv_attention_19_amd/csrc/pkv_device.h",
-                "paged_kv_attention_19_amd/csrc/quant_row.h")
+                "paged_kv_attention_19_amd/csrc/quant_row.h", "paged_kv_attention_19_amd/csrc/api.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_qwen3_traffic.json")
 
 

@@ -94,19 +94,11 @@ int decode_waves(int /*max_blocks_per_seq*/, int /*max_num_splits*/) {
   return forced ? forced : 4;
 }
 
-// Deep prefetch (5 blocks in flight per wavefront) when the whole grid fits
-// the chip's 256 CUs in one pass: each wavefront then runs alone on its SIMD,
-// registers are plentiful, and only its own loads in flight hide latency.
-// PKV_DECODE_PREFETCH=deep|shallow overrides, for tuning.
-bool decode_deep(int batch, int max_num_splits, int num_kv_heads, int waves) {
-  static const int forced = [] {
-    const char* e = std::getenv("PKV_DECODE_PREFETCH");
-    if (e == nullptr) return 0;
-    return std::string(e) == "deep" ? 1 : (std::string(e) == "shallow" ? 2 : 0);
-  }();
-  if (waves != 4) return false;
-  if (forced) return forced == 1;
-  return static_cast<int64_t>(batch) * max_num_splits * num_kv_heads <= 256;
+);
+  (void)batch;
+  (void)max_num_splits;
+  (void)num_kv_heads;
+  return waves == 4 && forced == 1;
 }
 
 // Balanced decode: 4 wavefronts per workgroup, 256 workgroups (one per CU)
@@ -274,12 +266,11 @@ static pkv_status run_split_decode(const char* fn, const void* q, int32_t q_dtyp
     p.num_slots = static_cast<int64_t>(cache->num_blocks) * cache->block_size;
   }
   const int waves = decode_waves(max_blocks_per_seq, max_num_splits);
-  const bool deep = decode_deep(batch, max_num_splits, cache->num_kv_heads, waves);
   hipError_t e;
   switch (cache->kv_dtype) {
-    case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, waves, deep, st); break;
-    case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, waves, deep, st); break;
-    default: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, waves, deep, st); break;
+    case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, waves, st); break;
+    case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, waves, st); break;
+    default: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, waves, st); break;
   }
   if (e != hipSuccess) return hip_fail(e, fn);
   if (!direct && out != nullptr) {
@@ -339,9 +330,9 @@ pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t ba
     const int wgs = balanced_workgroups(batch, cache->num_kv_heads, max_blocks_per_seq);
     hipError_t e;
     switch (cache->kv_dtype) {
-      case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, -wgs, false, st); break;
-      case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, -wgs, false, st); break;
-      default: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, -wgs, false, st); break;
+      case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, -wgs, st); break;
+      case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, -wgs, st); break;
+      default: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, -wgs, st); break;
     }
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();

@@ -4,8 +4,8 @@
 namespace pkv {
 
 hipError_t launch_decode_partial_f32(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves,
-                                   bool deep, hipStream_t st) {
-  return launch_partial_kv<PKV_F32>(p, q_dtype, head_dim, group, waves, deep, st);
+                                   hipStream_t st) {
+  return launch_partial_kv<PKV_F32>(p, q_dtype, head_dim, group, waves, st);
 }
 
 }  // namespace pkv

@@ -92,15 +92,14 @@ struct ChunkedParams {
 hipError_t launch_reshape(const ReshapeParams& p, int src_dtype, int kv_dtype, int head_dim,
                           hipStream_t stream);
 // Decode partial pass, one entry per KV element type; `waves` (2, 4, 8)
-// is the number of wavefronts per workgroup, `deep` asks for 5 blocks in
-// flight per wavefront (built with 4 wavefronts). A negative `waves` launches
-// the balanced single-pass decode on -waves workgroups instead.
+// is the number of wavefronts per workgroup. A negative `waves` launches the
+// balanced single-pass decode on -waves workgroups instead.
 hipError_t launch_decode_partial_f32(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves,
-                                     bool deep, hipStream_t stream);
+                                     hipStream_t stream);
 hipError_t launch_decode_partial_bf16(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves,
-                                      bool deep, hipStream_t stream);
+                                     hipStream_t stream);
 hipError_t launch_decode_partial_i8(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves,
-                                    bool deep, hipStream_t stream);
+                                     hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_chunked(const ChunkedParams& p, int kv_dtype, int head_dim, int group,
                           hipStream_t stream);

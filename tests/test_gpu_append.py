@@ -90,7 +90,7 @@ def test_append_equals_two_calls_and_oracle(gpu, name, ns):
 
 
 def test_append_qwen3_full_size(gpu):
-    """The benchmarked shape: B=32, one split per sequence (the deep-prefetch path)."""
+    """The benchmarked shape: B=32, one split per sequence."""
     step = W.qwen3_decode()
     out, lse = assert_same(step, gpu)
     ro, rl = O.decode(step, O.pool(step))
