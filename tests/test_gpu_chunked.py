@@ -92,3 +92,17 @@ def test_chunked_bad_metadata_gives_nan(gpu):
                                         G.ints(ctx, gpu), float(step.scale)).cpu().numpy()
     assert np.isnan(out[:80]).all()
     assert O.compare(out[80:], ro[80:])["ok"]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("Hq,Hkv", [(16, 8), (16, 4), (16, 2)])
+def test_multi_token_decode_rows(gpu, kv, Hq, Hkv):
+    """The speculative-verification shape: 2..8 new rows per sequence over
+    paged histories of very different lengths (one sequence of exactly q_len
+    tokens), GQA-packed, through the chunked entry point: row r of a q_len-row
+    step sits at position n - q_len + r."""
+    ctx = [300, 77, 1025, 8, 129, 2000]
+    ql = [2, 4, 8, 8, 5, 7]
+    step = W.make_step(f"mtd_{kv}_{Hq}_{Hkv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,
+                       kv_dtype=kv, src_dtype="bf16", seed=95 + Hkv)
+    run_and_check(step, gpu)
