@@ -187,8 +187,8 @@ class Replica:
         eb, sb = {"f32": (4, 0), "bf16": (2, 0), "i8": (1, 4)}[step.kv_dtype]
         self.kv_bytes = self.tokens * kv_bytes_per_token(step.num_kv_heads, step.head_dim, eb, sb)
         self.batch = B
-        # one pass writes the new rows too (split mode, one split per sequence)
-        self.fused = fuse and not balanced and self.max_ns == 1
+        # the decode launch writes the new rows too (split mode)
+        self.fused = fuse and not balanced
         src_eb = {"f32": 4, "bf16": 2}[step.src_dtype]
         self.append_bytes = B * (kv_bytes_per_token(step.num_kv_heads, step.head_dim, src_eb)
                                  + kv_bytes_per_token(step.num_kv_heads, step.head_dim, eb, sb))
@@ -210,8 +210,12 @@ class Replica:
 
     def partials(self):
         import paged_kv_attention_19_amd as pkv
-        if self.fused:
+        if self.fused and self.max_ns <= 1:
             self.decode_append()
+        elif self.fused:
+            pkv.paged_attention_decode_append(self.new_k, self.new_v, self.new_slots, self.q, self.cache,
+                                              self.tables, self.ctx, self.ns, self.max_ns, float(self.step.scale),
+                                              workspace=self.ws, partials_only=True)
         elif self.max_ns <= 1:
             self.decode()
         else:

@@ -287,10 +287,11 @@ def paged_attention_decode_append(k_new: torch.Tensor, v_new: torch.Tensor, slot
                                   context_lens: torch.Tensor, num_splits: torch.Tensor | None,
                                   max_num_splits: int, scale: float, out: torch.Tensor | None = None,
                                   out_lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                                  return_lse: bool = False):
+                                  return_lse: bool = False, partials_only: bool = False):
     """:func:`reshape_and_cache` of the step's new rows ``[B][Hkv][D]`` (one per
     sequence, at ``slot_mapping``) followed by :func:`paged_attention_decode`,
-    in one pass. Split mode only (``max_num_splits >= 1``)."""
+    in one pass. Split mode only (``max_num_splits >= 1``); ``partials_only``
+    as for :func:`paged_attention_decode`."""
     _need(q, "q", (torch.float32, torch.bfloat16), 3)
     B, Hq, D = q.shape
     _need(k_new, "k_new", (torch.float32, torch.bfloat16), 3)
@@ -310,15 +311,20 @@ def paged_attention_decode_append(k_new: torch.Tensor, v_new: torch.Tensor, slot
         _need(num_splits, "num_splits", (torch.int32,), 1)
         if num_splits.shape[0] != B:
             raise ValueError("num_splits batch mismatch")
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    _need(out, "out", (torch.float32,), 3)
-    if tuple(out.shape) != (B, Hq, D):
-        raise ValueError("out shape")
-    if out_lse is None and return_lse:
-        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    if out_lse is not None:
-        _need(out_lse, "out_lse", (torch.float32,), 2)
+    if partials_only:
+        if max_num_splits < 2 or workspace is None:
+            raise ValueError("partials_only needs max_num_splits > 1 and a workspace")
+        out = out_lse = None
+    else:
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        _need(out, "out", (torch.float32,), 3)
+        if tuple(out.shape) != (B, Hq, D):
+            raise ValueError("out shape")
+        if out_lse is None and return_lse:
+            out_lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        if out_lse is not None:
+            _need(out_lse, "out_lse", (torch.float32,), 2)
     need = decode_workspace_bytes(B, Hq, D, max_num_splits) if max_num_splits > 0 else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -327,8 +333,13 @@ def paged_attention_decode_append(k_new: torch.Tensor, v_new: torch.Tensor, slot
     _check(lib().pkv_paged_attention_decode_append(
         k_new.data_ptr(), v_new.data_ptr(), _CODE[k_new.dtype], slot_mapping.data_ptr(),
         q.data_ptr(), _CODE[q.dtype], B, Hq, ctypes.byref(d), block_tables.data_ptr(), block_tables.shape[1],
-        context_lens.data_ptr(), _ptr(num_splits), max_num_splits, float(scale), out.data_ptr(),
+        context_lens.data_ptr(), _ptr(num_splits), max_num_splits, float(scale), _ptr(out),
         _ptr(out_lse), _ptr(workspace), ws_bytes, _stream_handle()))
+    if partials_only:
+        f = workspace.view(torch.float32)
+        n_o = B * max_num_splits * Hq * D
+        return (f[:n_o].view(B, max_num_splits, Hq, D),
+                f[n_o:n_o + B * max_num_splits * Hq].view(B, max_num_splits, Hq))
     return (out, out_lse) if (return_lse or out_lse is not None) else out
 
 

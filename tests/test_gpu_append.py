@@ -121,3 +121,31 @@ def test_append_repeated_is_idempotent(gpu):
     out2, lse2 = run_append(step, cache, gpu)
     assert G.cache_bytes(cache) == b1
     assert out1.tobytes() == out2.tobytes() and lse1.tobytes() == lse2.tobytes()
+
+
+def test_append_partials_only_then_combine(gpu):
+    """Partials-only mode: the pass writes the new rows and the per-split
+    partials; lse_combine over them gives the one-call result bit for bit."""
+    step = W.make_step("pa", [300, 77, 1, 16, 129], [1] * 5, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                       kv_dtype="bf16", src_dtype="bf16", seed=55, num_blocks=80)
+    ns = 3
+    cache_a = G.build_cache(step, gpu, with_new=False)
+    out_a, lse_a = run_append(step, cache_a, gpu, num_splits=ns)
+    q, tables, ctx, nsv = step.decode_batch()
+    nsv = np.full_like(nsv, ns)
+    kn, vn, sl = decode_new_rows(step)
+    cache_b = G.build_cache(step, gpu, with_new=False)
+    ws = torch.empty(G.pkv.decode_workspace_bytes(len(ctx), step.num_q_heads, step.head_dim, ns),
+                     dtype=torch.uint8, device=gpu)
+    G.announce(f"decode_append partials_only B={len(ctx)} ns={ns}")
+    o_part, l_part = G.pkv.paged_attention_decode_append(
+        G.tensor(kn, step.src_dtype, gpu), G.tensor(vn, step.src_dtype, gpu), G.ints(sl, gpu, torch.int64),
+        G.tensor(q, step.q_dtype, gpu), cache_b, G.ints(tables, gpu), G.ints(ctx, gpu), G.ints(nsv, gpu), ns,
+        float(step.scale), workspace=ws, partials_only=True)
+    out_b, lse_b = G.pkv.lse_combine(o_part, l_part, G.ints(nsv, gpu))
+    torch.cuda.synchronize()
+    ba, bb = G.cache_bytes(cache_a), G.cache_bytes(cache_b)
+    for name in bb:
+        assert ba[name] == bb[name], name
+    assert out_b.cpu().numpy().tobytes() == out_a.tobytes()
+    assert lse_b.cpu().numpy().tobytes() == lse_a.tobytes()
