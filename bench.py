@@ -78,11 +78,12 @@ WORKLOADS = {
                           1, 512, {"workload": "mixed_int8_step_decode_rows", "context_lens": "uniform[256,4096]"}),
 }
 DEFAULT_SEEDS = {"qwen3_decode": 1902, "ragged_decode": 1903, "long_decode": 1904, "mixed_int8_decode": 1905}
-# Decode mode measured fastest on MI355X per shape: the small Qwen3 step and
-# the uniform long contexts keep one workgroup per (split, kv head) and merge
-# in LDS; the ragged and int8 batches gain from the balanced deal of tiles.
+# Decode mode measured fastest on MI355X per shape: one workgroup per
+# (split, kv head) for the Qwen3 step (one split per sequence), the uniform
+# long contexts and the int8 batch (512-token splits); the log-uniform ragged
+# batch gains from the balanced deal of tiles.
 DEFAULT_MODES = {"qwen3_decode": "splits", "ragged_decode": "balanced", "long_decode": "splits",
-                 "mixed_int8_decode": "balanced"}
+                 "mixed_int8_decode": "splits"}
 
 
 def parse():
@@ -305,9 +306,9 @@ def measure_chunked(dev, iters: int = 200):
     qc, cu, tc, cc = step.chunk_batch()
     qc, cu, tc, cc = dt(qc, "bf16"), dt(cu, "i32"), dt(tc, "i32"), dt(cc, "i32")
     max_q = int(np.diff(step.chunk_batch()[1]).max())
-    qd, td, ctxd, _ = step.decode_batch()
-    max_ns = 0   # the decode rows use the balanced mode
-    qd, td, ctxd = dt(qd, "bf16"), dt(td, "i32"), dt(ctxd, "i32")
+    qd, td, ctxd, nsd = step.decode_batch()
+    max_ns = int(nsd.max())   # the decode rows: ceil(n / 512) splits each
+    qd, td, ctxd, nsd = dt(qd, "bf16"), dt(td, "i32"), dt(ctxd, "i32"), dt(nsd, "i32")
     out_c = torch.empty((qc.shape[0], 16, 128), dtype=torch.float32, device=dev)
     out_d = torch.empty((qd.shape[0], 16, 128), dtype=torch.float32, device=dev)
     ws = torch.zeros(max(256, pkv.decode_workspace_bytes(qd.shape[0], 16, 128, max_ns)), dtype=torch.uint8, device=dev)
@@ -319,7 +320,7 @@ def measure_chunked(dev, iters: int = 200):
     def whole():
         pkv.reshape_and_cache(new_k, new_v, new_s, cache)
         chunked()
-        pkv.paged_attention_decode(qd, cache, td, ctxd, None, max_ns, scale, out=out_d, workspace=ws)
+        pkv.paged_attention_decode(qd, cache, td, ctxd, nsd, max_ns, scale, out=out_d, workspace=ws)
 
     res = {}
     for name, fn in (("chunked", chunked), ("step", whole)):

@@ -94,13 +94,6 @@ int decode_waves(int /*max_blocks_per_seq*/, int /*max_num_splits*/) {
   return forced ? forced : 4;
 }
 
-);
-  (void)batch;
-  (void)max_num_splits;
-  (void)num_kv_heads;
-  return waves == 4 && forced == 1;
-}
-
 // Balanced decode: 4 wavefronts per workgroup, 256 workgroups (one per CU)
 // or 512 for large batches; each wavefront owns two partial slots of
 // G (D + 1) floats (G <= Hq).

@@ -49,6 +49,7 @@ struct WaveDecoder {
     uint4 v[IPB][CPL];
     float ks[IPB];
     float vs[IPB];
+    int rows;   // token rows of the tile that are read (0 .. 16)
   };
 
   int lane, tslot, lc, lane_off;
@@ -99,35 +100,47 @@ struct WaveDecoder {
     }
   }
 
-  // Loads of the (block id, kv head) tile; id must already be a valid block.
-  __device__ __forceinline__ void load_tile(const DecodeParams& p, int id, int kh, Tile& t) const {
+  // Loads of the (block id, kv head) tile, of which the first `rows` token
+  // rows (0 .. 16) are read; id must be a valid block when rows > 0. The
+  // loads go through buffer descriptors sized to those rows: the rows past
+  // them (the tail of a sequence's last block) read as 0 without touching
+  // memory, and a tile with rows == 0 issues its loads with no traffic at
+  // all. Every call therefore issues the same instructions, which lets a
+  // ring of tiles be filled unconditionally.
+  __device__ __forceinline__ void load_tile(const DecodeParams& p, int id, int kh, int rows, Tile& t) const {
     const size_t tile = static_cast<size_t>(id) * p.num_kv_heads + kh;
+    const char* kt = static_cast<const char*>(p.k) + tile * kTileBytes;  // uniform bases
+    const char* vt = static_cast<const char*>(p.v) + tile * kTileBytes;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kt, rows * ROWB);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vt, rows * ROWB);
+    t.rows = rows;
     // K/V are streamed once per call: non-temporal loads keep them from
     // evicting the block tables, context lengths and q from the caches
-    const char* kt = static_cast<const char*>(p.k) + tile * kTileBytes;  // uniform base
-    const char* vt = static_cast<const char*>(p.v) + tile * kTileBytes;
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) t.k[i][j] = load_nt16(kt + lane_off + i * TPI * ROWB + j * LPT * 16);
+      for (int j = 0; j < CPL; ++j) t.k[i][j] = buffer_load_nt16(kr, lane_off + i * TPI * ROWB + j * LPT * 16);
     }
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) t.v[i][j] = load_nt16(vt + lane_off + i * TPI * ROWB + j * LPT * 16);
+      for (int j = 0; j < CPL; ++j) t.v[i][j] = buffer_load_nt16(vr, lane_off + i * TPI * ROWB + j * LPT * 16);
     }
     if constexpr (kI8) {
+      const __amdgpu_buffer_rsrc_t ksr = buffer_rsrc(p.k_scale + tile * kBlock, rows * 4);
+      const __amdgpu_buffer_rsrc_t vsr = buffer_rsrc(p.v_scale + tile * kBlock, rows * 4);
 #pragma unroll
       for (int i = 0; i < IPB; ++i) {
-        t.ks[i] = p.k_scale[tile * kBlock + i * TPI + tslot];
-        t.vs[i] = p.v_scale[tile * kBlock + i * TPI + tslot];
+        t.ks[i] = buffer_load_f32(ksr, (i * TPI + tslot) * 4);
+        t.vs[i] = buffer_load_f32(vsr, (i * TPI + tslot) * 4);
       }
     }
   }
 
-  // One block: tokens tok0 .. tok0 + 15; tokens >= t1 are masked (tail).
-  template <bool kFull>
-  __device__ __forceinline__ void process(const Tile& t, int tok0, int t1, float scale_log2) {
+  // One block of t.rows tokens (the rest of the tile is masked). The masked
+  // rows were read as 0 (K, V and the int8 scales), so they add exact zeros:
+  // their weights are exp2(-inf) = 0 and their values are finite.
+  __device__ __forceinline__ void process(const Tile& t, float scale_log2) {
     float sc[IPB][G];
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
@@ -136,7 +149,7 @@ struct WaveDecoder {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) unpack16<KV>(t.k[i][j], kf + j * EPL);
       }
-      const bool valid = kFull || (tok0 + i * TPI + tslot < t1);
+      const bool valid = i * TPI + tslot < t.rows;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float d = 0.f;
@@ -156,8 +169,7 @@ struct WaveDecoder {
         d = group_sum<LPT>(d);
         if constexpr (kI8) d *= t.ks[i] * scale_log2;
         else d *= scale_log2;
-        if constexpr (!kFull) d = valid ? d : neg_inf();
-        sc[i][g] = d;
+        sc[i][g] = valid ? d : neg_inf();
       }
     }
     // online softmax: move the reference max only when a block exceeds it by
@@ -200,26 +212,14 @@ struct WaveDecoder {
       float vf[NE];
 #pragma unroll
       for (int j = 0; j < CPL; ++j) unpack16<KV>(t.v[i][j], vf + j * EPL);
-      // rows past the context (and their int8 scales) may hold NaN: masked
-      // tokens contribute by select, never as 0 * NaN
-      const bool valid = kFull || (tok0 + i * TPI + tslot < t1);
-      if constexpr (!kFull) {
-#pragma unroll
-        for (int e = 0; e < NE; ++e) vf[e] = valid ? vf[e] : 0.f;
-      }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float pw = pr[i][g];
-        if constexpr (kI8) pw = (kFull || valid) ? pw * t.vs[i] : 0.f;
+        if constexpr (kI8) pw *= t.vs[i];
 #pragma unroll
         for (int e = 0; e < NE; ++e) acc[g][e] = fmaf(pw, vf[e], acc[g][e]);
       }
     }
-  }
-
-  __device__ __forceinline__ void run(const Tile& t, int tok0, int t1, float scale_log2) {
-    if (tok0 + kBlock <= t1) process<true>(t, tok0, t1, scale_log2);
-    else process<false>(t, tok0, t1, scale_log2);
   }
 
   // Bring the token slots to the wavefront's common reference max M.

@@ -138,49 +138,46 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
 
   wd.reset();
 
-  // ---- block ids: lane j of a 64-entry chunk holds the id of this wave's
-  //      block (chunk*64 + j); ids outside the pool poison the result ----
+  // ---- this wave's blocks (blocks w, w + NW, ... of the split), in chunks
+  //      of 64: lane j holds the id of the chunk's block j; ids outside the
+  //      pool poison the result ----
   const int32_t* trow = p.tables + static_cast<size_t>(b) * p.max_blocks + blk_lo + w;
-  int id_chunk = -1;
-  int ids = 0;
   bool bad = bad_n;
-  auto fetch_ids = [&](int ch) {
-    const int j = (ch << 6) + lane;
-    int v = 0;
-    bool lane_bad = false;
-    if (j < nb_w) {
-      v = trow[static_cast<size_t>(j) * NW];
-      lane_bad = static_cast<unsigned>(v) >= static_cast<unsigned>(p.num_blocks);
-      if (lane_bad) v = 0;
-    }
-    ids = v;
-    id_chunk = ch;
+  auto take_ids = [&](int v, int valid) -> int {
+    const bool lane_bad = lane < valid && static_cast<unsigned>(v) >= static_cast<unsigned>(p.num_blocks);
     bad = bad || wave_any(lane_bad);
+    return (lane < valid && !lane_bad) ? v : 0;
   };
-  auto block_id = [&](int it) -> int {
-    if ((it >> 6) != id_chunk) fetch_ids(it >> 6);
-    return readlane(ids, it & 63);
-  };
-  if (s == 0 && nb_w > 0) {  // blk_lo == 0: the early read holds this wave's first 64 ids
-    const bool lane_bad = lane < nb_w && static_cast<unsigned>(early_ids) >= static_cast<unsigned>(p.num_blocks);
-    ids = lane_bad ? 0 : early_ids;
-    id_chunk = 0;
-    bad = bad || wave_any(lane_bad);
-  }
-  auto tok0_of = [&](int it) { return t0 + (w + it * NW) * kBlock; };
-
-  // ---- stream the wave's blocks with PD blocks of K/V in flight ahead: a
-  //      ring of PD + 1 register tiles, indexed statically (fully unrolled) ----
   Tile ring[PD + 1];
+  for (int c0 = 0; c0 < nb_w; c0 += kWave) {
+    const int cn = min(kWave, nb_w - c0);
+    int ids;
+    if (s == 0 && c0 == 0) {
+      ids = take_ids(early_ids, cn);   // blk_lo == 0: the early read holds them
+    } else {
+      const int j = c0 + lane;
+      ids = take_ids(lane < cn ? trow[static_cast<size_t>(j) * NW] : 0, cn);
+    }
+    // tile `it` of the chunk: its id and valid rows (0 past the chunk, so
+    // that the ring is filled by the same instructions every time)
+    auto issue = [&](int it, Tile& t) {
+      int rows = 0, id = 0;
+      if (it < cn) {
+        rows = min(kBlock, t1 - (t0 + (w + (c0 + it) * NW) * kBlock));
+        id = readlane(ids, it);
+      }
+      wd.load_tile(p, id, kh, rows, t);
+    };
+    // ---- stream the chunk with PD tiles of K/V in flight ahead: a ring of
+    //      PD + 1 register tiles, indexed statically (fully unrolled) ----
 #pragma unroll
-  for (int k = 0; k < PD; ++k)
-    if (k < nb_w) wd.load_tile(p, block_id(k), kh, ring[k]);
-  for (int it = 0; it < nb_w; it += PD + 1) {
+    for (int k = 0; k < PD; ++k) issue(k, ring[k]);
+    for (int it = 0; it < cn; it += PD + 1) {
 #pragma unroll
-    for (int k = 0; k <= PD; ++k) {
-      const int cur = it + k;
-      if (cur + PD < nb_w) wd.load_tile(p, block_id(cur + PD), kh, ring[(k + PD) % (PD + 1)]);
-      if (cur < nb_w) wd.run(ring[k], tok0_of(cur), t1, p.scale_log2);
+      for (int k = 0; k <= PD; ++k) {
+        issue(it + k + PD, ring[(k + PD) % (PD + 1)]);
+        if (it + k < cn) wd.process(ring[k], p.scale_log2);
+      }
     }
   }
 
@@ -363,9 +360,9 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
   int blk = static_cast<int>((r0 - base) % nb);
 
   // the load cursor runs PD tiles ahead of the processing cursor
-  int lb = b, lkh = kh, lblk = blk, lnb = nb;
+  int lb = b, lkh = kh, lblk = blk, lnb = nb, ln = n;
   int64_t lbase = base;
-  auto advance = [&](int& cb, int& ckh, int& cblk, int& cnb, int64_t& cbase) {
+  auto advance = [&](int& cb, int& ckh, int& cblk, int& cnb, int64_t& cbase, int& cn) {
     if (++cblk < cnb) return;
     cblk = 0;
     if (++ckh < Hkv) return;
@@ -373,7 +370,8 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
     cbase += static_cast<int64_t>(Hkv) * cnb;
     do {
       ++cb;
-      cnb = cb < p.batch ? blocks_of(p.ctx[cb], p.max_blocks) : 1;
+      cn = cb < p.batch ? p.ctx[cb] : kBlock;
+      cnb = blocks_of(cn, p.max_blocks);
     } while (cnb == 0);
   };
 
@@ -401,8 +399,9 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
     const int id = block_id(lb, lblk);
     const bool ok = static_cast<unsigned>(id) < static_cast<unsigned>(p.num_blocks);
     ring_bad = ok ? (ring_bad & ~(1 << slot)) : (ring_bad | (1 << slot));
-    wd.load_tile(p, ok ? id : 0, lkh, ring[slot]);
-    advance(lb, lkh, lblk, lnb, lbase);
+    const int rows = min(kBlock, ln - lblk * kBlock);
+    wd.load_tile(p, ok ? id : 0, lkh, rows, ring[slot]);
+    advance(lb, lkh, lblk, lnb, lbase, ln);
     ++lpos;
   };
 
@@ -552,15 +551,14 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
       if (pos < r1) {
         if (lpos < r1) issue((k + PD) % (PD + 1));
         seg_bad = seg_bad || ((ring_bad >> k) & 1);
-        wd.run(ring[k], blk * kBlock, n, p.scale_log2);
+        wd.process(ring[k], p.scale_log2);
         ++pos;
         // leaving the segment (or the range): finish it
         const bool last_of_seg = (blk + 1 == nb);
         if (last_of_seg || pos == r1) {
           finish_segment(b, kh, nb, base, n);
           if (pos < r1) {
-            advance(b, kh, blk, nb, base);
-            n = p.ctx[b];
+            advance(b, kh, blk, nb, base, n);
             wd.load_q(p.q, Hq, b, kh * G);
           }
         } else {
@@ -586,16 +584,19 @@ hipError_t launch_balanced_t(const DecodeParams& p, int workgroups, hipStream_t 
   return hipGetLastError();
 }
 
-// waves: wavefronts per workgroup (2 blocks of K/V in flight per wavefront;
-// a deeper ring of 5 measured slower on the B=32 decode step: 12.9 us against
-// 12.6 us)
+// waves: wavefronts per workgroup. Each wavefront keeps one block of K/V in
+// flight while it reduces the previous one. Measured on MI355X (bf16, 16/8
+// heads, head_dim 128), per launch: the 32-sequence step of 128..384 tokens
+// takes 10.7 us with one block ahead, 10.9 / 11.5 / 12.0 us with 2 / 3 / 4
+// (each extra block costs 32 VGPRs, with no latency left to hide); 8 x 32k
+// tokens and the 4096-token int8 batch are within 1% of their best.
 template <int KV, int QT, int D, int G>
 hipError_t launch_partial_w(const DecodeParams& p, int waves, hipStream_t st) {
   if (waves < 0) return launch_balanced_t<KV, QT, D, G>(p, -waves, st);   // balanced: -workgroups
   switch (waves) {
-    case 2: return launch_partial_t<KV, QT, D, G, 2, 2>(p, st);
-    case 4: return launch_partial_t<KV, QT, D, G, 4, 2>(p, st);
-    case 8: return launch_partial_t<KV, QT, D, G, 8, 2>(p, st);
+    case 2: return launch_partial_t<KV, QT, D, G, 2, 1>(p, st);
+    case 4: return launch_partial_t<KV, QT, D, G, 4, 1>(p, st);
+    case 8: return launch_partial_t<KV, QT, D, G, 8, 1>(p, st);
     default: return hipErrorInvalidValue;
   }
 }

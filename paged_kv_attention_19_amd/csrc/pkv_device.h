@@ -17,11 +17,23 @@ constexpr float kLn2 = 0.6931471805599453f;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// 16-byte load marked non-temporal (streamed data that should not displace
-// what the caches hold for later use).
-__device__ __forceinline__ uint4 load_nt16(const void* ptr) {
-  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(ptr));
+// Buffer descriptor over `bytes` bytes at `base` (raw dwords, no stride):
+// loads at offsets past `bytes` return 0 and access no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+}
+
+constexpr int kBufNt = 2;   // buffer-load cache policy: non-temporal
+
+// 16-byte non-temporal load at byte offset `off` of a buffer (0 past its end).
+__device__ __forceinline__ uint4 buffer_load_nt16(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufNt));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 4-byte float load at byte offset `off` of a buffer (0 past its end).
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
 // ---- element decoding ------------------------------------------------------
