@@ -25,18 +25,22 @@ pin would say "parity unpinned" here; there are none.
 from .paged_attention import (  # noqa: F401
     BF16,
     F32,
+    FP8,
     I8,
     NAN_BF16_BITS,
+    NAN_FP8_CODE,
     OraclePool,
     attend_direct,
     bf16_bits_to_f64,
     decode_rows,
+    fp8_e4m3_value,
     gather_kv,
     kv_head_of,
     lse_combine,
     online_softmax_attend,
     paged_chunked,
     paged_decode,
+    quantize_rows_fp8,
     quantize_rows_int8,
     reshape_and_cache,
     split_bounds,

@@ -1,4 +1,4 @@
-"""Float64 NumPy oracle: scatter, gather, direct softmax attention, int8 quantizer.
+"""Float64 NumPy oracle: scatter, gather, direct softmax attention, int8 and fp8 quantizers.
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``): never imported by the
 product path.
@@ -34,6 +34,14 @@ reason, in the design notes of the repository):
   ``scale = amax / 127`` in float32, ``code = clamp(rint(x / scale), -127, 127)``
   with an IEEE float32 division and round-half-to-even; ``amax == 0`` gives
   ``scale = 1``. The dequantized value is ``code * scale``.
+* FP8 KV (the course README's curriculum, S00 "bf16/fp8" with S08
+  quantization) is read as the OCP 8-bit floating-point format E4M3 (sign, 4
+  exponent bits with bias 7, 3 mantissa bits; exponent 0 holds the subnormals
+  ``m * 2^-9``; ``S.1111.111`` is NaN; no infinities; largest finite 448),
+  scaled like the int8 cache: per (token, KV head), ``scale = amax / 448`` in
+  float32 (``amax == 0`` gives 1) and ``code`` = the E4M3 value nearest to the
+  float32 quotient ``x / scale``, ties to the even code, saturating at 448. The
+  dequantized value is ``value(code) * scale``.
 * Split-K uses block-aligned contiguous ranges:
   ``tps = bs * ceil(ceil(n / ns) / bs)``, split ``s`` covers
   ``[s * tps, min(n, (s + 1) * tps))``; an empty split yields
@@ -43,7 +51,7 @@ reason, in the design notes of the repository):
 
 Layouts (the same as the library's public header states):
 ``k, v : [num_blocks][Hkv][block_size][D]`` in the storage dtype;
-``k_scale, v_scale : [num_blocks][Hkv][block_size]`` float32 (int8 only);
+``k_scale, v_scale : [num_blocks][Hkv][block_size]`` float32 (int8 and fp8 only);
 ``block_tables : int32 [B][max_blocks]`` (``-1`` past the used entries);
 ``slot_mapping : int64 [T]``, slot ``s`` is block ``s // bs``, offset ``s % bs``;
 a negative slot means "skip this row".
@@ -59,12 +67,16 @@ import numpy as np
 F32 = "f32"
 BF16 = "bf16"
 I8 = "i8"
+FP8 = "fp8"
 
 # A quiet NaN in bfloat16 storage: unused pool rows are filled with it so that a
 # stray read shows up as NaN in the output.
 NAN_BF16_BITS = np.uint16(0x7FC0)
 
-_STORAGE = {F32: np.float32, BF16: np.uint16, I8: np.int8}
+_STORAGE = {F32: np.float32, BF16: np.uint16, I8: np.int8, FP8: np.uint8}
+
+# An E4M3 NaN code: unused fp8 pool rows hold it (and NaN scales).
+NAN_FP8_CODE = np.uint8(0x7F)
 
 
 # --------------------------------------------------------------------------
@@ -79,13 +91,30 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def fp8_e4m3_value(code) -> np.ndarray:
+    """Value of OCP E4M3 codes, float64: sign bit 7, exponent bits 6..3 (bias
+    7), mantissa bits 2..0. Exponent 0 holds the subnormals ``m * 2^-9``; a
+    nonzero exponent gives ``(1 + m / 8) * 2^(e - 7)``; ``S.1111.111`` is NaN
+    and there are no infinities."""
+    c = np.asarray(code, np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.power(2.0, e - 7))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+# the finite non-negative E4M3 values, codes 0x00 .. 0x7E, in increasing order
+_FP8_POSITIVE = fp8_e4m3_value(np.arange(0x7F))
+
+
 def decode_rows(raw: np.ndarray, dtype: str, scale: np.ndarray | None = None) -> np.ndarray:
     """Storage values -> float64.
 
-    int8 rows are dequantized as ``code * scale`` with the per-(token, head)
-    float32 scale broadcast over the last (head_dim) axis. The product of an
-    8-bit integer and a float32 needs at most 24 + 7 significant bits, so it is
-    exact in float64.
+    int8 and fp8 rows are dequantized as ``value(code) * scale`` with the
+    per-(token, head) float32 scale broadcast over the last (head_dim) axis. The
+    product of an 8-bit integer (or an E4M3 value) and a float32 needs at most
+    24 + 7 significant bits, so it is exact in float64.
     """
     if dtype == F32:
         return np.asarray(raw, dtype=np.float32).astype(np.float64)
@@ -94,6 +123,11 @@ def decode_rows(raw: np.ndarray, dtype: str, scale: np.ndarray | None = None) ->
     if dtype == I8:
         assert scale is not None, "int8 rows need their scales"
         return np.asarray(raw, np.int8).astype(np.float64) * np.asarray(scale, np.float32).astype(np.float64)[..., None]
+    if dtype == FP8:
+        # an E4M3 value has at most 4 significant bits: its product with a
+        # float32 scale is exact in float64
+        assert scale is not None, "fp8 rows need their scales"
+        return fp8_e4m3_value(raw) * np.asarray(scale, np.float32).astype(np.float64)[..., None]
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -115,6 +149,28 @@ def quantize_rows_int8(x32: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     scale = (safe / np.float32(127.0)).astype(np.float32)   # amax == 0 -> scale 1
     quot = (x32 / scale[..., None]).astype(np.float32)
     codes = np.clip(np.rint(quot), -127.0, 127.0).astype(np.int8)
+    return codes, scale
+
+
+def quantize_rows_fp8(x32: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Quantize float32 rows (last axis = head_dim) to OCP E4M3 codes + float32
+    scale: ``scale = amax / 448`` (IEEE float32 division; ``amax == 0`` gives
+    1), then each float32 quotient ``x / scale`` takes the code of the nearest
+    finite E4M3 value, found by search over the value table; an exact tie goes
+    to the even code; quotients past 448 take 448. The sign bit is the
+    quotient's."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=-1)
+    safe = np.where(amax > np.float32(0.0), amax, np.float32(448.0)).astype(np.float32)
+    scale = (safe / np.float32(448.0)).astype(np.float32)   # amax == 0 -> scale 1
+    y = (x32 / scale[..., None]).astype(np.float32)
+    a = np.abs(y).astype(np.float64)                          # exact
+    hi = np.minimum(np.searchsorted(_FP8_POSITIVE, a, side="left"), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = np.abs(a - _FP8_POSITIVE[lo])
+    d_hi = np.abs(_FP8_POSITIVE[hi] - a)
+    pick = np.where(d_hi < d_lo, hi, np.where(d_lo < d_hi, lo, np.where(hi % 2 == 0, hi, lo)))
+    codes = (pick | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
     return codes, scale
 
 
@@ -149,6 +205,11 @@ class OraclePool:
             self.v = np.zeros(shape, np.int8)
             self.k_scale = np.full(shape[:3], np.nan, np.float32)
             self.v_scale = np.full(shape[:3], np.nan, np.float32)
+        elif self.kv_dtype == FP8:
+            self.k = np.full(shape, NAN_FP8_CODE, np.uint8)
+            self.v = np.full(shape, NAN_FP8_CODE, np.uint8)
+            self.k_scale = np.full(shape[:3], np.nan, np.float32)
+            self.v_scale = np.full(shape[:3], np.nan, np.float32)
         else:
             raise ValueError(self.kv_dtype)
 
@@ -164,7 +225,8 @@ def reshape_and_cache(pool: OraclePool, k_new: np.ndarray, v_new: np.ndarray,
     Append-then-attend (page "llm-inference", section "KV Cache"): the rows of
     the new tokens go into the cache before attention reads them. A negative
     slot skips its row. Float caches take the source bytes unchanged (the
-    source dtype must match); the int8 cache quantizes each (token, head) row.
+    source dtype must match); the int8 and fp8 caches quantize each (token,
+    head) row.
     """
     slots = np.asarray(slot_mapping, dtype=np.int64)
     T = slots.shape[0]
@@ -185,8 +247,9 @@ def reshape_and_cache(pool: OraclePool, k_new: np.ndarray, v_new: np.ndarray,
         assert src_dtype in (F32, BF16)
         k32 = decode_rows(k_new, src_dtype).astype(np.float32)[live]  # exact: bf16 and f32 fit binary32
         v32 = decode_rows(v_new, src_dtype).astype(np.float32)[live]
-        kc, ks = quantize_rows_int8(k32)
-        vc, vs = quantize_rows_int8(v32)
+        quantize = quantize_rows_int8 if pool.kv_dtype == I8 else quantize_rows_fp8
+        kc, ks = quantize(k32)
+        vc, vs = quantize(v32)
         pool.k[blk, :, off, :] = kc
         pool.v[blk, :, off, :] = vc
         pool.k_scale[blk, :, off] = ks
@@ -207,9 +270,9 @@ def gather_kv(pool: OraclePool, table_row: np.ndarray, n: int) -> tuple[np.ndarr
     off = t % bs
     assert ((blk >= 0) & (blk < pool.num_blocks)).all(), "block id out of range"
     # advanced indices on axes 0 and 2 -> result axes [n][Hkv][D]
-    if pool.kv_dtype == I8:
-        K = decode_rows(pool.k[blk, :, off, :], I8, pool.k_scale[blk, :, off])
-        V = decode_rows(pool.v[blk, :, off, :], I8, pool.v_scale[blk, :, off])
+    if pool.kv_dtype in (I8, FP8):
+        K = decode_rows(pool.k[blk, :, off, :], pool.kv_dtype, pool.k_scale[blk, :, off])
+        V = decode_rows(pool.v[blk, :, off, :], pool.kv_dtype, pool.v_scale[blk, :, off])
     else:
         K = decode_rows(pool.k[blk, :, off, :], pool.kv_dtype)
         V = decode_rows(pool.v[blk, :, off, :], pool.kv_dtype)

@@ -42,6 +42,11 @@ MUTANTS = {
     "combine_no_shift": ("w = np.where(live, np.exp(np.where(live, lse_parts, M) - M), 0.0)",
                          "w = np.where(live, np.exp(np.where(live, lse_parts, M)), 0.0) * 0 + live"),
     "split_not_block_aligned": ("tps = block_size * (-(-per // block_size))", "tps = per"),
+    "fp8_bias_8": ("(1.0 + m / 8.0) * np.power(2.0, e - 7)", "(1.0 + m / 8.0) * np.power(2.0, e - 8)"),
+    "fp8_subnormal_step": ("np.where(e == 0, m * 2.0 ** -9,", "np.where(e == 0, m * 2.0 ** -10,"),
+    "fp8_ties_to_odd": ("np.where(hi % 2 == 0, hi, lo)", "np.where(hi % 2 == 0, lo, hi)"),
+    "fp8_truncate": ("pick = np.where(d_hi < d_lo, hi,", "pick = np.where(d_hi < 0, hi,"),
+    "fp8_scale_over_240": ("(safe / np.float32(448.0))", "(safe / np.float32(240.0))"),
 }
 
 # every pin, with the arguments its pytest parametrisation would give it
@@ -51,6 +56,11 @@ PIN_CALLS = [
     (pins.test_quantizer_against_exact_rational_arithmetic, ()),
     (pins.test_quantizer_bounds_and_special_cases, ()),
     (pins.test_quantizer_near_half_way_quotients, ()),
+    (pins.test_fp8_decoding_matches_format, ()),
+    (pins.test_fp8_decoding_matches_library, ()),
+    (pins.test_fp8_encoder_matches_library_rounding, ()),
+    (pins.test_fp8_quantizer_bounds_and_special_cases, ()),
+    (pins.test_fp8_scatter_stores_quantized_rows, ()),
     (pins.test_gather_of_scatter_is_identity, ("f32",)),
     (pins.test_gather_of_scatter_is_identity, ("bf16",)),
     (pins.test_int8_scatter_stores_quantized_rows, ()),

@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import BF16, F32, I8, OraclePool
+from oracle import BF16, F32, FP8, I8, OraclePool
 from workloads import f32_to_bf16_bits, make_step, tiny_decode
 
 # --------------------------------------------------------------------------
@@ -229,6 +229,106 @@ def test_quantizer_bounds_and_special_cases():
 
 
 # --------------------------------------------------------------------------
+# fp8 (OCP E4M3) decoding and quantizer
+# --------------------------------------------------------------------------
+
+# E4M3 values worked out by hand from the format: sign | exponent (4 bits,
+# bias 7) | mantissa (3 bits); exponent 0 -> m * 2^-9.
+FP8_WORKED = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2.0 ** -6,
+              0x38: 1.0, 0x39: 1.125, 0x40: 2.0, 0x1D: 0.1015625, 0x77: 240.0, 0x7E: 448.0,
+              0xB8: -1.0, 0xC4: -3.0, 0xFE: -448.0, 0x81: -(2.0 ** -9)}
+
+
+def test_fp8_decoding_matches_format():
+    v = oracle.fp8_e4m3_value(np.arange(256))
+    for c, want in FP8_WORKED.items():
+        assert v[c] == want, hex(c)
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and int(np.isnan(v).sum()) == 2
+    assert v[0x80] == 0.0 and math.copysign(1.0, v[0x80]) == -1.0
+    assert (np.diff(v[:0x7F]) > 0).all()                        # codes 0 .. 0x7E increase
+    assert np.array_equal(v[0x80:0xFF], -v[:0x7F])              # the sign bit negates
+    # spacing: 2^-9 below 2^-6 (subnormals and the first binade), then 2^(e-10)
+    assert np.allclose(np.diff(v[:0x10]), 2.0 ** -9)
+
+
+def test_fp8_decoding_matches_library():
+    """torch's float8_e4m3fn (the same OCP format) decodes all 256 codes alike."""
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    lib = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = oracle.fp8_e4m3_value(np.arange(256))
+    assert np.array_equal(np.isnan(lib), np.isnan(ours))
+    fin = ~np.isnan(ours)
+    assert np.array_equal(lib[fin], ours[fin]) and np.array_equal(np.signbit(lib[fin]), np.signbit(ours[fin]))
+
+
+def _fp8_codes_with_unit_scale(x: np.ndarray) -> np.ndarray:
+    """Quantize values with |x| <= 448 through rows led by 448 (scale exactly 1)."""
+    rows = np.concatenate([np.full((len(x), 1), 448.0, np.float32), np.asarray(x, np.float32)[:, None]], axis=1)
+    codes, scale = oracle.quantize_rows_fp8(rows)
+    assert (scale == 1.0).all()
+    return codes[:, 1]
+
+
+def test_fp8_encoder_matches_library_rounding():
+    """torch rounds float32 to float8_e4m3fn to nearest, ties to even: on every
+    value of magnitude <= 448 the oracle's table search must give its codes,
+    including exact midpoints between neighbours and the float32 values next to
+    them."""
+    import torch
+    rng = np.random.default_rng(12)
+    mags = np.exp2(rng.uniform(-13, np.log2(448.0), 20000))
+    x = (mags * rng.choice([-1.0, 1.0], 20000)).astype(np.float32)
+    pos = oracle.fp8_e4m3_value(np.arange(0x7F))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)        # exact in float32
+    assert np.array_equal(mids.astype(np.float64), (pos[:-1] + pos[1:]) / 2)
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))])
+    x = np.concatenate([x, near, -near, [0.0, -0.0, 448.0, -448.0]]).astype(np.float32)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(_fp8_codes_with_unit_scale(x), lib)
+
+
+def test_fp8_quantizer_bounds_and_special_cases():
+    rng = np.random.default_rng(13)
+    x = f32_to_bf16_bits(rng.standard_normal((500, 128), dtype=np.float32))
+    x32 = oracle.bf16_bits_to_f64(x).astype(np.float32)
+    codes, scale = oracle.quantize_rows_fp8(x32)
+    assert not np.isnan(oracle.fp8_e4m3_value(codes)).any()
+    y = x32.astype(np.float64) / scale[:, None].astype(np.float64)      # exact quotient
+    err = np.abs(y - oracle.fp8_e4m3_value(codes))
+    # half a step of the format (relative 2^-4 from 2^-6 up, absolute 2^-10 below),
+    # plus the float32 rounding of the quotient (2^-24 relative)
+    bound = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) * (1 + 2.0 ** -20)
+    assert (err <= bound).all()
+    # the element of largest magnitude maps to +-448 with its sign
+    j = np.argmax(np.abs(x32), axis=1)
+    r = np.arange(500)
+    assert (codes[r, j] & 0x7F == 0x7E).all()
+    assert ((codes[r, j] >> 7) == (x32[r, j] < 0)).all()
+    # all-zero row -> scale 1, codes 0
+    c0, s0 = oracle.quantize_rows_fp8(np.zeros((1, 8), np.float32))
+    assert s0[0] == 1.0 and (c0 == 0).all()
+    # worked values at scale 1: 0.1 -> 1.625 * 2^-4 (0x1D); 2^-10 ties to 0; 3 * 2^-11
+    # -> 2^-9; 432 (between 416 and 448) ties to the even code 0x7E
+    got = _fp8_codes_with_unit_scale(np.array([0.1, 2.0 ** -10, 3 * 2.0 ** -11, 432.0, -432.0, 1.0], np.float32))
+    assert got.tolist() == [0x1D, 0x00, 0x01, 0x7E, 0xFE, 0x38]
+
+
+def test_fp8_scatter_stores_quantized_rows():
+    step = make_step("f8", [20, 33], [4, 1], num_q_heads=4, num_kv_heads=2, head_dim=16,
+                     q_dtype=BF16, kv_dtype=FP8, src_dtype=BF16, seed=14)
+    pool = oracle_pool(step)
+    for i, n in enumerate(step.context_lens):
+        K, V = oracle.gather_kv(pool, step.block_tables[i], int(n))
+        Kc, Vc = (oracle.decode_rows(x, BF16) for x in step.kv_contiguous(i))
+        kc, ks = oracle.quantize_rows_fp8(Kc.astype(np.float32))
+        assert np.array_equal(K, oracle.fp8_e4m3_value(kc) * ks.astype(np.float64)[..., None])
+        # dequantized rows are within half a step of the source
+        tol = np.maximum(np.abs(Vc) * 2.0 ** -4, 2.0 ** -10 * np.abs(Vc).max(axis=-1, keepdims=True) / 448)
+        assert (np.abs(V - Vc) <= tol * (1 + 2.0 ** -16)).all()
+
+
+# --------------------------------------------------------------------------
 # scatter / gather (claims s06 and s11)
 # --------------------------------------------------------------------------
 
@@ -264,7 +364,7 @@ def test_int8_scatter_stores_quantized_rows():
         assert (np.abs(V - Vc) <= (0.5 + 2.0 ** -16) * vs).all()
 
 
-@pytest.mark.parametrize("kv_dtype", [BF16, I8])
+@pytest.mark.parametrize("kv_dtype", [BF16, I8, FP8])
 def test_piecewise_chunk_writes_equal_one_shot(kv_dtype):
     """Claim s11: writing a chunk's K/V in pieces yields a bit-identical cache."""
     step = make_step("pieces", [300, 77], [300, 77], num_q_heads=4, num_kv_heads=2, head_dim=32,
@@ -297,7 +397,7 @@ def test_negative_slots_are_skipped_and_bad_slots_raise():
         oracle.gather_kv(pool, np.array([0]), 5)          # 5 tokens in one 4-slot block
 
 
-@pytest.mark.parametrize("kv_dtype", [F32, I8])
+@pytest.mark.parametrize("kv_dtype", [F32, I8, FP8])
 def test_output_invariant_under_block_placement(kv_dtype):
     """Claim s06: the result does not depend on where blocks sit in the pool."""
     kw = dict(num_q_heads=4, num_kv_heads=2, head_dim=32, q_dtype=F32 if kv_dtype == F32 else BF16,

@@ -28,7 +28,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-F32, BF16, I8 = "f32", "bf16", "i8"
+F32, BF16, I8, FP8 = "f32", "bf16", "i8", "fp8"
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -63,7 +63,7 @@ class Step:
     block_size: int
     num_blocks: int
     q_dtype: str
-    kv_dtype: str            # cache storage dtype: f32, bf16 or i8
+    kv_dtype: str            # cache storage dtype: f32, bf16, i8 or fp8
     src_dtype: str           # dtype of the K/V rows handed to reshape_and_cache
     scale: np.float32
     context_lens: np.ndarray  # int32 [S]
@@ -146,7 +146,7 @@ def make_step(name: str, context_lens, q_lens, *, num_q_heads: int, num_kv_heads
     S = len(ctx)
     assert ql.shape == (S,) and (ql >= 1).all() and (ql <= ctx).all()
     Hq, Hkv, D, bs = num_q_heads, num_kv_heads, head_dim, block_size
-    src_dtype = src_dtype or (kv_dtype if kv_dtype != I8 else BF16)
+    src_dtype = src_dtype or (kv_dtype if kv_dtype not in (I8, FP8) else BF16)
     nblk = -(-ctx // bs)
     need = int(nblk.sum())
     num_blocks = need if num_blocks is None else int(num_blocks)
@@ -267,8 +267,9 @@ def long_decode(batch: int = 8, context_len: int = 32768, num_splits: int = 64,
 
 def mixed_int8(num_prefill: int = 4, chunk: int = 512, prefix: int = 1536, num_decode: int = 124,
                lo: int = 256, hi: int = 4096, max_tokens_per_split: int = 512,
-               seed: int = 1905) -> Step:
-    """Mixed chunked-prefill + decode step over an int8 KV cache: ``num_prefill``
+               seed: int = 1905, kv_dtype: str = I8) -> Step:
+    """Mixed chunked-prefill + decode step over an int8 (or, with ``kv_dtype=
+    "fp8"``, an fp8) KV cache: ``num_prefill``
     sequences with a ``chunk``-row causal chunk after a ``prefix``-token cached
     prefix, plus ``num_decode`` decode rows with n uniform in [256, 4096].
     16q/8kv/128, q and the new K/V rows bf16 (quantized by the cache write),
@@ -277,6 +278,7 @@ def mixed_int8(num_prefill: int = 4, chunk: int = 512, prefix: int = 1536, num_d
     dec = rng.integers(lo, hi, size=num_decode, endpoint=True)
     ctx = np.concatenate([np.full(num_prefill, prefix + chunk), dec]).astype(np.int64)
     ql = np.concatenate([np.full(num_prefill, chunk), np.ones(num_decode)]).astype(np.int64)
-    return make_step("mixed_int8", ctx, ql, num_q_heads=16, num_kv_heads=8, head_dim=128,
-                     q_dtype=BF16, kv_dtype=I8, src_dtype=BF16,
+    assert kv_dtype in (I8, FP8)
+    return make_step("mixed_int8" if kv_dtype == I8 else "mixed_fp8", ctx, ql, num_q_heads=16, num_kv_heads=8,
+                     head_dim=128, q_dtype=BF16, kv_dtype=kv_dtype, src_dtype=BF16,
                      num_splits=splits_for(ctx, max_tokens_per_split), seed=seed)
