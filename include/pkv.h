@@ -55,14 +55,16 @@ typedef int32_t pkv_status;
 #define PKV_F32 0   /* IEEE binary32 */
 #define PKV_BF16 1  /* bfloat16 (upper half of a binary32) */
 #define PKV_I8 2    /* int8 code with a float32 scale per (token, kv head) */
+#define PKV_FP8 3   /* OCP FP8 E4M3 code with a float32 scale per (token, kv head) */
 
 /*
  * The KV block pool.
  *   k, v       : [num_blocks][num_kv_heads][block_size][head_dim] row-major,
  *                elements of kv_dtype. One (block, head) tile is contiguous.
  *   k_scale,
- *   v_scale    : [num_blocks][num_kv_heads][block_size] float32 for PKV_I8,
- *                NULL otherwise. Stored value = code * scale.
+ *   v_scale    : [num_blocks][num_kv_heads][block_size] float32 for PKV_I8
+ *                and PKV_FP8, NULL otherwise. Stored value = value(code) * scale,
+ *                value(code) the integer for I8, the E4M3 value for FP8.
  * Token t of a sequence lives in block block_table[t / block_size] at offset
  * t % block_size; slot s of the pool is block s / block_size, offset
  * s % block_size.
@@ -97,6 +99,11 @@ const char* pkv_version(void);
  *   scale = amax / 127 (IEEE float32 division; amax == 0 gives scale 1),
  *   code = clamp(rint(x / scale), -127, 127) with an IEEE division and
  *   round-half-to-even (course README, curriculum S08 quantization).
+ *   The FP8 cache (course README, curriculum S00 bf16/fp8) takes F32 or BF16
+ *   rows and scales them the same way with scale = amax / 448; code = the OCP
+ *   E4M3 value nearest to the float32 quotient x / scale, ties to the even
+ *   code, saturating at 448 (E4M3: sign, 4 exponent bits with bias 7, 3
+ *   mantissa bits, subnormals m * 2^-9, S.1111.111 NaN, no infinities).
  *   Two rows with the same slot in one call: undefined which one lands.
  *   Writing a chunk in pieces gives the same bytes as writing it at once
  *   (course README, claim s11).
@@ -205,7 +212,7 @@ pkv_status pkv_paged_attention_decode_append(const void* k_new, const void* v_ne
  *   the cached tokens t <= n_i - L_i + r (bottom-right aligned causal mask).
  *   out          : float32 [total_q][num_q_heads][head_dim]; out_lse float32
  *                  [total_q][num_q_heads] or NULL (natural log).
- *   Cache dtypes: BF16 or I8; head_dim 128; GQA group size in {1, 2, 4, 8}.
+ *   Cache dtypes: BF16, I8 or FP8; head_dim 128; GQA group size in {1, 2, 4, 8}.
  *   A chunk longer than max_q_len or than its context yields NaN rows.
  */
 pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t num_seqs,

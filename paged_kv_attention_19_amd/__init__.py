@@ -23,14 +23,15 @@ from dataclasses import dataclass
 import torch
 
 __all__ = [
-    "F32", "BF16", "I8", "PkvError", "KVCache", "lib", "library_path", "exported_symbols",
+    "F32", "BF16", "I8", "FP8", "PkvError", "KVCache", "lib", "library_path", "exported_symbols",
     "reshape_and_cache", "decode_workspace_bytes", "paged_attention_decode",
     "paged_attention_decode_append", "paged_attention_chunked", "lse_combine", "version",
 ]
 
-F32, BF16, I8 = 0, 1, 2
-_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
-_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8}
+F32, BF16, I8, FP8 = 0, 1, 2, 3
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8, FP8: torch.float8_e4m3fn}
+_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.float8_e4m3fn: FP8}
+_SCALED = (I8, FP8)   # 8-bit codes with a float32 scale per (token, kv head)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_HERE), "include", "pkv.h")
@@ -136,7 +137,8 @@ def _need(t: torch.Tensor, name: str, dtypes, ndim: int | None = None, device=No
 @dataclass
 class KVCache:
     """The block pool: ``k, v [num_blocks][num_kv_heads][block_size][head_dim]``,
-    plus ``k_scale, v_scale [num_blocks][num_kv_heads][block_size]`` float32 for int8."""
+    plus ``k_scale, v_scale [num_blocks][num_kv_heads][block_size]`` float32 for
+    int8 and fp8 (OCP E4M3, stored as ``torch.float8_e4m3fn``)."""
 
     k: torch.Tensor
     v: torch.Tensor
@@ -166,13 +168,17 @@ class KVCache:
     @classmethod
     def allocate(cls, num_blocks: int, num_kv_heads: int, head_dim: int, kv_dtype: int,
                  device="cuda", block_size: int = 16, fill_nan: bool = True) -> "KVCache":
-        """Allocate a pool; float rows (int8: the scales) start as NaN so that a
-        read of an unwritten row shows up in the output."""
+        """Allocate a pool; float rows (int8 and fp8: the scales; fp8 codes too)
+        start as NaN so that a read of an unwritten row shows up in the output."""
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
         dt = _TORCH_DTYPE[kv_dtype]
-        if kv_dtype == I8:
-            k = torch.zeros(shape, dtype=dt, device=device)
-            v = torch.zeros(shape, dtype=dt, device=device)
+        if kv_dtype in _SCALED:
+            if kv_dtype == FP8:   # 0x7F is an E4M3 NaN
+                k = torch.full(shape, 0x7F if fill_nan else 0, dtype=torch.uint8, device=device).view(dt)
+                v = torch.full(shape, 0x7F if fill_nan else 0, dtype=torch.uint8, device=device).view(dt)
+            else:
+                k = torch.zeros(shape, dtype=dt, device=device)
+                v = torch.zeros(shape, dtype=dt, device=device)
             fill = float("nan") if fill_nan else 1.0
             ks = torch.full(shape[:3], fill, dtype=torch.float32, device=device)
             vs = torch.full(shape[:3], fill, dtype=torch.float32, device=device)
@@ -182,21 +188,21 @@ class KVCache:
 
     def descriptor(self) -> _Cache:
         for name in ("k", "v"):
-            _need(getattr(self, name), f"cache.{name}", (torch.float32, torch.bfloat16, torch.int8), 4)
+            _need(getattr(self, name), f"cache.{name}", tuple(_CODE), 4)
         if self.v.shape != self.k.shape or self.v.dtype != self.k.dtype:
             raise ValueError("cache.k and cache.v differ in shape or dtype")
-        if self.kv_dtype == I8:
+        if self.kv_dtype in _SCALED:
             for name in ("k_scale", "v_scale"):
                 t = getattr(self, name)
                 if t is None:
-                    raise ValueError(f"int8 cache needs {name}")
+                    raise ValueError(f"int8 / fp8 cache needs {name}")
                 _need(t, f"cache.{name}", (torch.float32,), 3)
                 if tuple(t.shape) != tuple(self.k.shape[:3]):
                     raise ValueError(f"cache.{name} shape {tuple(t.shape)} != {tuple(self.k.shape[:3])}")
         return _Cache(self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim, self.kv_dtype,
                       self.k.data_ptr(), self.v.data_ptr(),
-                      _ptr(self.k_scale) if self.kv_dtype == I8 else None,
-                      _ptr(self.v_scale) if self.kv_dtype == I8 else None)
+                      _ptr(self.k_scale) if self.kv_dtype in _SCALED else None,
+                      _ptr(self.v_scale) if self.kv_dtype in _SCALED else None)
 
 
 def reshape_and_cache(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,

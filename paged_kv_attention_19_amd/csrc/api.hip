@@ -42,6 +42,7 @@ const char* dtype_name(int d) {
     case PKV_F32: return "F32";
     case PKV_BF16: return "BF16";
     case PKV_I8: return "I8";
+    case PKV_FP8: return "FP8";
     default: return "?";
   }
 }
@@ -56,12 +57,13 @@ pkv_status check_cache(const pkv_cache* c, const char* fn) {
   if (c->block_size != 16) return fail(PKV_ERR_UNSUPPORTED, "%s: block_size=%d (built: 16)", fn, c->block_size);
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim=%d (built: 64, 128)", fn, c->head_dim);
-  if (c->kv_dtype != PKV_F32 && c->kv_dtype != PKV_BF16 && c->kv_dtype != PKV_I8)
-    return fail(PKV_ERR_INVALID_ARG, "%s: kv_dtype=%d is not F32/BF16/I8", fn, c->kv_dtype);
-  if (c->kv_dtype == PKV_I8 && (c->k_scale == nullptr || c->v_scale == nullptr))
-    return fail(PKV_ERR_INVALID_ARG, "%s: I8 cache needs k_scale and v_scale", fn);
+  if (c->kv_dtype != PKV_F32 && c->kv_dtype != PKV_BF16 && c->kv_dtype != PKV_I8 && c->kv_dtype != PKV_FP8)
+    return fail(PKV_ERR_INVALID_ARG, "%s: kv_dtype=%d is not F32/BF16/I8/FP8", fn, c->kv_dtype);
+  const bool scaled = c->kv_dtype == PKV_I8 || c->kv_dtype == PKV_FP8;
+  if (scaled && (c->k_scale == nullptr || c->v_scale == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "%s: %s cache needs k_scale and v_scale", fn, dtype_name(c->kv_dtype));
   if (!aligned16(c->k) || !aligned16(c->v)) return fail(PKV_ERR_INVALID_ARG, "%s: cache k/v not 16-byte aligned", fn);
-  if (c->kv_dtype == PKV_I8 && ((reinterpret_cast<uintptr_t>(c->k_scale) | reinterpret_cast<uintptr_t>(c->v_scale)) & 3u))
+  if (scaled && ((reinterpret_cast<uintptr_t>(c->k_scale) | reinterpret_cast<uintptr_t>(c->v_scale)) & 3u))
     return fail(PKV_ERR_INVALID_ARG, "%s: scales not 4-byte aligned", fn);
   const int64_t tile_elems = static_cast<int64_t>(c->num_kv_heads) * c->block_size * c->head_dim;
   if (tile_elems * c->num_blocks > (int64_t(1) << 46))
@@ -127,9 +129,10 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, int32_t s
   if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0)
     return fail(PKV_ERR_INVALID_ARG, "%s: slot_mapping not 8-byte aligned", fn);
   const int kv = cache->kv_dtype;
-  if (kv == PKV_I8) {
+  if (kv == PKV_I8 || kv == PKV_FP8) {
     if (src_dtype != PKV_F32 && src_dtype != PKV_BF16)
-      return fail(PKV_ERR_INVALID_ARG, "%s: I8 cache takes F32 or BF16 rows, got %s", fn, dtype_name(src_dtype));
+      return fail(PKV_ERR_INVALID_ARG, "%s: %s cache takes F32 or BF16 rows, got %s", fn, dtype_name(kv),
+                  dtype_name(src_dtype));
   } else if (src_dtype != kv) {
     return fail(PKV_ERR_INVALID_ARG, "%s: %s cache needs %s rows, got %s", fn, dtype_name(kv), dtype_name(kv),
                 dtype_name(src_dtype));
@@ -263,7 +266,8 @@ static pkv_status run_split_decode(const char* fn, const void* q, int32_t q_dtyp
   switch (cache->kv_dtype) {
     case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, waves, st); break;
     case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, waves, st); break;
-    default: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, waves, st); break;
+    case PKV_I8: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, waves, st); break;
+    default: e = pkv::launch_decode_partial_fp8(p, q_dtype, D, group, waves, st); break;
   }
   if (e != hipSuccess) return hip_fail(e, fn);
   if (!direct && out != nullptr) {
@@ -325,7 +329,8 @@ pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t ba
     switch (cache->kv_dtype) {
       case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, -wgs, st); break;
       case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, -wgs, st); break;
-      default: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, -wgs, st); break;
+      case PKV_I8: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, -wgs, st); break;
+      default: e = pkv::launch_decode_partial_fp8(p, q_dtype, D, group, -wgs, st); break;
     }
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
@@ -356,9 +361,10 @@ pkv_status pkv_paged_attention_decode_append(const void* k_new, const void* v_ne
   if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0)
     return fail(PKV_ERR_INVALID_ARG, "%s: slot_mapping not 8-byte aligned", fn);
   const int kv = cache->kv_dtype;
-  if (kv == PKV_I8) {
+  if (kv == PKV_I8 || kv == PKV_FP8) {
     if (src_dtype != PKV_F32 && src_dtype != PKV_BF16)
-      return fail(PKV_ERR_INVALID_ARG, "%s: I8 cache takes F32 or BF16 rows, got %s", fn, dtype_name(src_dtype));
+      return fail(PKV_ERR_INVALID_ARG, "%s: %s cache takes F32 or BF16 rows, got %s", fn, dtype_name(kv),
+                  dtype_name(src_dtype));
   } else if (src_dtype != kv) {
     return fail(PKV_ERR_INVALID_ARG, "%s: %s cache needs %s rows, got %s", fn, dtype_name(kv), dtype_name(kv),
                 dtype_name(src_dtype));
@@ -408,7 +414,7 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
   if (num_seqs == 0) return ok();
   if (q_dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "%s: q_dtype=%s (built: BF16)", fn, dtype_name(q_dtype));
   if (cache->kv_dtype == PKV_F32)
-    return fail(PKV_ERR_UNSUPPORTED, "%s: F32 cache (built: BF16, I8)", fn);
+    return fail(PKV_ERR_UNSUPPORTED, "%s: F32 cache (built: BF16, I8, FP8)", fn);
   if (cache->head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim=%d (built: 128)", fn, cache->head_dim);
   if (q == nullptr || cu_q_lens == nullptr || block_tables == nullptr || context_lens == nullptr || out == nullptr)
     return fail(PKV_ERR_INVALID_ARG, "%s: q/cu_q_lens/block_tables/context_lens/out is NULL", fn);

@@ -40,8 +40,9 @@
 // loads whose range is the valid part of each block: rows past the context
 // and blocks outside the table come back as zeros with no branch, so every
 // tile issues the same loads and only the older set is waited for. An int8
-// cache is dequantized on its way to LDS (codes are exact in bf16): the K
-// scale multiplies the score column, the V scale the weight.
+// or fp8 cache is dequantized on its way to LDS (int8 codes and E4M3 values
+// are exact in bf16): the K scale multiplies the score column, the V scale
+// the weight.
 #include <type_traits>
 #include <utility>
 
@@ -90,6 +91,21 @@ __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int byte0) {
   return pack_bf16(a, b);
 }
 
+// Codes B0, B0 + 1 (B0 = 0 or 2) of a scaled 8-bit cache word -> two
+// bfloat16: int8 integers, or OCP E4M3 values (gfx950's conversion decodes
+// them exactly; at most 4 significant bits and exponents -9 .. 8, so the bf16
+// packing is exact too).
+template <int KV, int B0>
+__device__ __forceinline__ uint32_t code_pair_to_bf16x2(uint32_t w) {
+  static_assert(B0 == 0 || B0 == 2, "an aligned pair of bytes");
+  if constexpr (KV == PKV_I8) {
+    return i8pair_to_bf16x2(w, B0);
+  } else {
+    const f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), B0 == 2);
+    return pack_bf16(f.x, f.y);
+  }
+}
+
 // Raw buffer over `bytes` bytes at `base`: loads at or past `bytes` return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, kRsrcWord3);
@@ -101,21 +117,21 @@ __device__ __forceinline__ uint4 lds_read16(const char* a) { return *reinterpret
 // stored to LDS. A thread stages part of its group's 32-token half of the
 // tile: tg = (thread % 256) / 16, u = thread % 16.
 struct Staged {
-  uint4 k[2];      // K chunk i: token tg + 16 i of the half, 16-byte unit u (int8: 8 bytes)
+  uint4 k[2];      // K chunk i: token tg + 16 i of the half, 16-byte unit u (8-bit codes: 8 bytes)
   uint4 v[2];      // V: tokens 2 tg and 2 tg + 1 of the half, unit u
-  float sc;        // int8: the K (thread % 64 < 32) or V scale of token thread % 32 of the half
+  float sc;        // 8-bit codes: the K (thread % 64 < 32) or V scale of token thread % 32 of the half
   bool sc_ok;      // that token exists
 };
 
 template <int KV, int G>
 __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   constexpr int P = kRows / G;               // positions per query tile
-  constexpr bool kI8 = (KV == PKV_I8);
+  constexpr bool kScaled = is_scaled_kv(KV);   // int8 / fp8 codes + a scale per row
   constexpr float kSlack = 8.0f;
-  constexpr int kRowBytes = kI8 ? kD : 2 * kD;   // bytes of one cached K or V row
+  constexpr int kRowBytes = kScaled ? kD : 2 * kD;   // bytes of one cached K or V row
   constexpr int kUnit = kRowBytes / 16;          // bytes of 8 dims of a cached row
   __shared__ __attribute__((aligned(16))) char s_kv[kStages][kStageBytes];
-  __shared__ __attribute__((aligned(16))) float s_sc[kStages][2 * kTile];   // int8: K scale x softmax scale, V scale
+  __shared__ __attribute__((aligned(16))) float s_sc[kStages][2 * kTile];   // 8-bit codes: K scale x softmax scale, V scale
   __shared__ __attribute__((aligned(16))) int s_ids[kIdsCached];
   static_assert(kStages * kStageBytes >= 4 * kMergeFloats * 64 * 4, "merge area");
 
@@ -242,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     ts.k[1] = rsrc(kpool + head_off + id1 * blk_stride, rk1 * kRowBytes);
     const bool v1 = (wl >> 1) != 0;
     ts.v = rsrc(vpool + head_off + (v1 ? id1 : id0) * blk_stride, (v1 ? rk1 : rk0) * kRowBytes);
-    if constexpr (kI8) {
+    if constexpr (kScaled) {
       // scale of token 32 th + (tl % 32): K for tl % 64 < 32, V otherwise
       const int t = tl & 31;
       const bool hi = t >= kBlock;
@@ -256,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   auto gissue = [&](const TileSrc& ts, Staged& st) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if constexpr (kI8) {
+      if constexpr (kScaled) {
         const u32x2v_t c = __builtin_bit_cast(u32x2v_t, __builtin_amdgcn_raw_buffer_load_b64(ts.k[i], koff, 0, 0));
         st.k[i] = make_uint4(c.x, c.y, 0, 0);
         const u32x2v_t d = __builtin_bit_cast(
@@ -270,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
         st.v[i] = make_uint4(d.x, d.y, d.z, d.w);
       }
     }
-    if constexpr (kI8) {
+    if constexpr (kScaled) {
       st.sc = *ts.sc;
       st.sc_ok = ts.sc_ok;
     }
@@ -286,11 +302,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   // V^T: dims 8 u + e, tokens 32 th + 2 tg, + 1 (4 bytes in unit 4 th + tg / 4)
   auto vw_off = [&](int e) { return kKBytes + vt_off(8 * u16 + e, 4 * th + (tg >> 2)) + ((tg & 3) << 2); };
 
-  // K chunk i of st -> bf16 (int8 codes converted)
+  // K chunk i of st -> bf16 (8-bit codes converted)
   auto k_bf16 = [&](const Staged& st, int i) -> uint4 {
-    if constexpr (kI8) {
-      return make_uint4(i8pair_to_bf16x2(st.k[i].x, 0), i8pair_to_bf16x2(st.k[i].x, 2),
-                        i8pair_to_bf16x2(st.k[i].y, 0), i8pair_to_bf16x2(st.k[i].y, 2));
+    if constexpr (kScaled) {
+      return make_uint4(code_pair_to_bf16x2<KV, 0>(st.k[i].x), code_pair_to_bf16x2<KV, 2>(st.k[i].x),
+                        code_pair_to_bf16x2<KV, 0>(st.k[i].y), code_pair_to_bf16x2<KV, 2>(st.k[i].y));
     } else {
       return st.k[i];
     }
@@ -299,11 +315,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   auto v_bf16 = [&](const Staged& st, uint32_t (&vw)[2][4]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if constexpr (kI8) {
-        vw[i][0] = i8pair_to_bf16x2(st.v[i].x, 0);
-        vw[i][1] = i8pair_to_bf16x2(st.v[i].x, 2);
-        vw[i][2] = i8pair_to_bf16x2(st.v[i].y, 0);
-        vw[i][3] = i8pair_to_bf16x2(st.v[i].y, 2);
+      if constexpr (kScaled) {
+        vw[i][0] = code_pair_to_bf16x2<KV, 0>(st.v[i].x);
+        vw[i][1] = code_pair_to_bf16x2<KV, 2>(st.v[i].x);
+        vw[i][2] = code_pair_to_bf16x2<KV, 0>(st.v[i].y);
+        vw[i][3] = code_pair_to_bf16x2<KV, 2>(st.v[i].y);
       } else {
         vw[i][0] = st.v[i].x;
         vw[i][1] = st.v[i].y;
@@ -317,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     return __builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
   };
   auto sc_store = [&](const Staged& st, int stage) {
-    if constexpr (kI8) {
+    if constexpr (kScaled) {
       // the 4 wavefronts of a group store the same values to the same places
       const float sc = st.sc_ok ? st.sc : 0.f;
       s_sc[stage][((tl & 32) ? kTile : 0) + 32 * th + (tl & 31)] = (tl & 32) ? sc : sc * p.scale_log2;
@@ -383,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     ka[2] = lds_read16(kb + kr_off[2]);
     float4 sc4;
     auto read_sc = [&](int t0) { sc4 = *reinterpret_cast<const float4*>(scs + t0); };
-    if constexpr (kI8) read_sc(tok_of(0));
+    if constexpr (kScaled) read_sc(tok_of(0));
     float sv[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) sv[v] = sacc[v];
@@ -398,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     for (int c = 0; c < 4; ++c) {
       mfma1(c);
       float kv[4];
-      if constexpr (kI8) {
+      if constexpr (kScaled) {
         kv[0] = sc4.x; kv[1] = sc4.y; kv[2] = sc4.z; kv[3] = sc4.w;
         read_sc(c < 3 ? tok_of(4 * (c + 1)) : kTile + tok_of(0));   // next: K scales, then V scales of scores 0..3
       }
@@ -406,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       for (int e = 0; e < 4; ++e) {
         const int v = 4 * c + e;
         float x = sv[v];
-        if constexpr (kI8) x *= kv[e];   // K scale x softmax scale
+        if constexpr (kScaled) x *= kv[e];   // K scale x softmax scale
         if constexpr (kDiag) {
           if (tok_of(v) > tlim) x = neg_inf();
         }
@@ -423,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       mfma1(4 + c);
       if (c == 0) {
         float tmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-        if constexpr (!kI8) tmax *= p.scale_log2;   // the max commutes with a positive scale
+        if constexpr (!kScaled) tmax *= p.scale_log2;   // the max commutes with a positive scale
         // move the reference max only when the tile exceeds it by more than
         // the slack: weights stay below 2^kSlack and O is rarely rescaled
         const bool need = tmax > m + kSlack;
@@ -433,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
         mu = (m == neg_inf()) ? 0.f : m;
       }
       float vv[4];
-      if constexpr (kI8) {
+      if constexpr (kScaled) {
         vv[0] = sc4.x; vv[1] = sc4.y; vv[2] = sc4.z; vv[3] = sc4.w;
         if (c < 3) read_sc(kTile + tok_of(4 * (c + 1)));
       }
@@ -443,10 +459,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
         float pw[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-          if constexpr (kI8) pw[k] = __builtin_amdgcn_exp2f(sv[v + k] - mu);
+          if constexpr (kScaled) pw[k] = __builtin_amdgcn_exp2f(sv[v + k] - mu);
           else pw[k] = __builtin_amdgcn_exp2f(fmaf(sv[v + k], p.scale_log2, -mu));
           rsum += pw[k];
-          if constexpr (kI8) pw[k] *= vv[e + k];
+          if constexpr (kScaled) pw[k] *= vv[e + k];
         }
         // high parts rounded to bf16, residuals exact in float32 then rounded
         const uint32_t hp = pack_bf16(pw[0], pw[1]);
@@ -627,6 +643,7 @@ hipError_t launch_chunked(const ChunkedParams& p, int kv_dtype, int head_dim, in
   if (head_dim != kD) return hipErrorNotSupported;
   if (kv_dtype == PKV_BF16) return launch_g<PKV_BF16>(p, group, st);
   if (kv_dtype == PKV_I8) return launch_g<PKV_I8>(p, group, st);
+  if (kv_dtype == PKV_FP8) return launch_g<PKV_FP8>(p, group, st);
   return hipErrorNotSupported;
 }
 

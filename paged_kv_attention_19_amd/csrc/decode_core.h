@@ -40,7 +40,7 @@ struct WaveDecoder {
   static constexpr int NE = CPL * EPL;                  // row elements per lane
   static constexpr int kTileBytes = kBlock * ROWB;
   static constexpr bool kDot2 = (KV == PKV_BF16 && QT == PKV_BF16);
-  static constexpr bool kI8 = (KV == PKV_I8);
+  static constexpr bool kScaled = is_scaled_kv(KV);   // int8 / fp8 code + scale per row
   static constexpr float kRescaleSlack = 8.0f;
   static_assert(TPI * LPT == kWave && IPB * TPI == kBlock && IPB * CPL * 1024 == kTileBytes, "geometry");
 
@@ -126,7 +126,7 @@ struct WaveDecoder {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) t.v[i][j] = buffer_load_nt16(vr, lane_off + i * TPI * ROWB + j * LPT * 16);
     }
-    if constexpr (kI8) {
+    if constexpr (kScaled) {
       const __amdgpu_buffer_rsrc_t ksr = buffer_rsrc(p.k_scale + tile * kBlock, rows * 4);
       const __amdgpu_buffer_rsrc_t vsr = buffer_rsrc(p.v_scale + tile * kBlock, rows * 4);
 #pragma unroll
@@ -138,7 +138,7 @@ struct WaveDecoder {
   }
 
   // One block of t.rows tokens (the rest of the tile is masked). The masked
-  // rows were read as 0 (K, V and the int8 scales), so they add exact zeros:
+  // rows were read as 0 (K, V and the 8-bit caches' scales), so they add exact zeros:
   // their weights are exp2(-inf) = 0 and their values are finite.
   __device__ __forceinline__ void process(const Tile& t, float scale_log2) {
     float sc[IPB][G];
@@ -167,7 +167,7 @@ struct WaveDecoder {
           for (int e = 0; e < NE; ++e) d = fmaf(qf[g][e], kf[e], d);
         }
         d = group_sum<LPT>(d);
-        if constexpr (kI8) d *= t.ks[i] * scale_log2;
+        if constexpr (kScaled) d *= t.ks[i] * scale_log2;
         else d *= scale_log2;
         sc[i][g] = valid ? d : neg_inf();
       }
@@ -215,7 +215,7 @@ struct WaveDecoder {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float pw = pr[i][g];
-        if constexpr (kI8) pw *= t.vs[i];
+        if constexpr (kScaled) pw *= t.vs[i];
 #pragma unroll
         for (int e = 0; e < NE; ++e) acc[g][e] = fmaf(pw, vf[e], acc[g][e]);
       }

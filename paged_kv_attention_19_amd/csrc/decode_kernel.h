@@ -30,13 +30,13 @@ namespace pkv {
 // Append (split mode): the whole wavefront writes the new K and V rows of kv
 // head kh of sequence b to slot p.slots[b] (skipped when the slot is outside
 // the pool), with the same per-row arithmetic as reshape_and_cache.
-template <int SRC, int D>
+template <int SRC, int D, int KV>
 __device__ __forceinline__ void append_quant(const DecodeParams& p, int64_t row, int64_t dst_row, int lane) {
   constexpr int R = D / KvGeom<SRC>::kEpl;   // lanes per row: K on lanes [0, R), V on [R, 2R)
   if (lane < 2 * R) {
     const bool isv = lane >= R;
-    quantize_row_piece<SRC, D>(isv ? p.v_new : p.k_new, isv ? p.v_w : p.k_w, isv ? p.v_scale_w : p.k_scale_w, row,
-                               dst_row, lane % R);
+    quantize_row_piece<SRC, D, KV>(isv ? p.v_new : p.k_new, isv ? p.v_w : p.k_w, isv ? p.v_scale_w : p.k_scale_w,
+                                   row, dst_row, lane % R);
   }
 }
 
@@ -46,9 +46,9 @@ __device__ __forceinline__ void append_rows(const DecodeParams& p, int b, int kh
   if (slot < 0 || slot >= p.num_slots) return;
   const int64_t row = static_cast<int64_t>(b) * p.num_kv_heads + kh;
   const int64_t dst_row = ((slot / kBlock) * p.num_kv_heads + kh) * kBlock + slot % kBlock;
-  if constexpr (KV == PKV_I8) {
-    if (p.new_dtype == PKV_BF16) append_quant<PKV_BF16, D>(p, row, dst_row, lane);
-    else append_quant<PKV_F32, D>(p, row, dst_row, lane);
+  if constexpr (is_scaled_kv(KV)) {
+    if (p.new_dtype == PKV_BF16) append_quant<PKV_BF16, D, KV>(p, row, dst_row, lane);
+    else append_quant<PKV_F32, D, KV>(p, row, dst_row, lane);
   } else {
     constexpr int kRowBytes = D * KvGeom<KV>::kEsize;
     constexpr int kPieces = kRowBytes / 16;

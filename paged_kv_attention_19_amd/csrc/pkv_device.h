@@ -16,6 +16,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Buffer descriptor over `bytes` bytes at `base` (raw dwords, no stride):
 // loads at offsets past `bytes` return 0 and access no memory.
@@ -60,13 +61,49 @@ __device__ __forceinline__ void unpack16(const uint4& x, float* f) {
       f[2 * i] = bf16_lo(w[i]);
       f[2 * i + 1] = bf16_hi(w[i]);
     }
-  } else {
+  } else if constexpr (KV == PKV_I8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) f[4 * i + b] = i8_at(w[i], b);
     }
+  } else {
+    // FP8: gfx950's conversion decodes the OCP E4M3 format exactly (two codes
+    // per instruction)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), false);
+      const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), true);
+      f[4 * i + 0] = lo.x;
+      f[4 * i + 1] = lo.y;
+      f[4 * i + 2] = hi.x;
+      f[4 * i + 3] = hi.y;
+    }
   }
+}
+
+// Caches that store an 8-bit code and a float32 scale per (token, kv head).
+constexpr bool is_scaled_kv(int kv) { return kv == PKV_I8 || kv == PKV_FP8; }
+
+// OCP FP8 E4M3 code of y: the nearest E4M3 value, ties to the even code,
+// saturating at 448 (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+// exponent field 0 holds the subnormals m * 2^-9). |y| is written as
+// q * 2^(e - 3) with e its binade exponent (at least -6, where the subnormals
+// share the 2^-9 step); q = rint(|y| * 2^(3 - e)), an exact power-of-two
+// scaling and one round-half-to-even, lands in [0, 16]; 16 carries into the
+// next binade.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.0f);
+  int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xffu) - 127;
+  e = e < -6 ? -6 : e;
+  float q = __builtin_rintf(__builtin_ldexpf(a, 3 - e));
+  if (q >= 16.0f) {
+    q = 8.0f;
+    ++e;
+  }
+  const uint32_t qi = static_cast<uint32_t>(q);
+  return sign | (qi < 8u ? qi : ((static_cast<uint32_t>(e + 7) << 3) | (qi - 8u)));
 }
 
 template <int KV>

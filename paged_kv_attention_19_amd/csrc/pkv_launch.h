@@ -100,6 +100,8 @@ hipError_t launch_decode_partial_bf16(const DecodeParams& p, int q_dtype, int he
                                      hipStream_t stream);
 hipError_t launch_decode_partial_i8(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves,
                                      hipStream_t stream);
+hipError_t launch_decode_partial_fp8(const DecodeParams& p, int q_dtype, int head_dim, int group, int waves,
+                                     hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_chunked(const ChunkedParams& p, int kv_dtype, int head_dim, int group,
                           hipStream_t stream);

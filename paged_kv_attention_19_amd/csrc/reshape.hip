@@ -6,8 +6,8 @@
 // K and the same piece of V; consecutive threads cover a row, so both the read
 // of the new rows and the write of each destination row are coalesced.
 //
-// Int8 cache: a group of D / EPL lanes quantizes one (token, head) row (the
-// shared row quantizer of quant_row.h).
+// Int8 and FP8 caches: a group of D / EPL lanes quantizes one (token, head)
+// row (the shared row quantizer of quant_row.h).
 #include "pkv_device.h"
 #include "pkv_launch.h"
 #include "quant_row.h"
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void reshape_copy_kernel(ReshapeParams p) {
       *reinterpret_cast<const uint4*>(static_cast<const char*>(p.v_new) + src);
 }
 
-template <int SRC, int D>
+template <int SRC, int D, int KV>
 __global__ __launch_bounds__(256) void reshape_quant_kernel(ReshapeParams p) {
   constexpr int R = D / KvGeom<SRC>::kEpl;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -56,8 +56,8 @@ __global__ __launch_bounds__(256) void reshape_quant_kernel(ReshapeParams p) {
   const int64_t blk = slot / kBlock;
   const int64_t off = slot % kBlock;
   const int64_t dst_row = (blk * p.num_kv_heads + h) * kBlock + off;
-  quantize_row_piece<SRC, D>(p.k_new, p.k, p.k_scale, row, dst_row, r);
-  quantize_row_piece<SRC, D>(p.v_new, p.v, p.v_scale, row, dst_row, r);
+  quantize_row_piece<SRC, D, KV>(p.k_new, p.k, p.k_scale, row, dst_row, r);
+  quantize_row_piece<SRC, D, KV>(p.v_new, p.v, p.v_scale, row, dst_row, r);
 }
 
 template <int KV, int D>
@@ -69,11 +69,11 @@ hipError_t launch_copy(const ReshapeParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int SRC, int D>
+template <int SRC, int D, int KV>
 hipError_t launch_quant(const ReshapeParams& p, hipStream_t st) {
   constexpr int R = D / KvGeom<SRC>::kEpl;
   const int64_t total = static_cast<int64_t>(p.num_tokens) * p.num_kv_heads * R;
-  hipLaunchKernelGGL((reshape_quant_kernel<SRC, D>), dim3(static_cast<uint32_t>((total + 255) / 256)), dim3(256),
+  hipLaunchKernelGGL((reshape_quant_kernel<SRC, D, KV>), dim3(static_cast<uint32_t>((total + 255) / 256)), dim3(256),
                      0, st, p);
   return hipGetLastError();
 }
@@ -82,8 +82,10 @@ template <int D>
 hipError_t launch_reshape_d(const ReshapeParams& p, int src, int kv, hipStream_t st) {
   if (kv == PKV_F32 && src == PKV_F32) return launch_copy<PKV_F32, D>(p, st);
   if (kv == PKV_BF16 && src == PKV_BF16) return launch_copy<PKV_BF16, D>(p, st);
-  if (kv == PKV_I8 && src == PKV_F32) return launch_quant<PKV_F32, D>(p, st);
-  if (kv == PKV_I8 && src == PKV_BF16) return launch_quant<PKV_BF16, D>(p, st);
+  if (kv == PKV_I8 && src == PKV_F32) return launch_quant<PKV_F32, D, PKV_I8>(p, st);
+  if (kv == PKV_I8 && src == PKV_BF16) return launch_quant<PKV_BF16, D, PKV_I8>(p, st);
+  if (kv == PKV_FP8 && src == PKV_F32) return launch_quant<PKV_F32, D, PKV_FP8>(p, st);
+  if (kv == PKV_FP8 && src == PKV_BF16) return launch_quant<PKV_BF16, D, PKV_FP8>(p, st);
   return hipErrorInvalidValue;
 }
 

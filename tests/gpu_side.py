@@ -11,7 +11,7 @@ import torch
 
 import paged_kv_attention_19_amd as pkv
 
-CODE = {"f32": pkv.F32, "bf16": pkv.BF16, "i8": pkv.I8}
+CODE = {"f32": pkv.F32, "bf16": pkv.BF16, "i8": pkv.I8, "fp8": pkv.FP8}
 
 
 def announce(msg: str) -> None:

@@ -74,6 +74,10 @@ STEPS = {
                                           head_dim=128, kv_dtype="i8", src_dtype="bf16", seed=52, num_blocks=60),
     "int8_from_f32_d64": lambda: W.make_step("a8f", [40, 33, 16], [1] * 3, num_q_heads=4, num_kv_heads=2,
                                              head_dim=64, q_dtype="f32", kv_dtype="i8", src_dtype="f32", seed=53),
+    "fp8_from_bf16": lambda: W.make_step("af8", [300, 77, 1, 16, 17], [1] * 5, num_q_heads=16, num_kv_heads=8,
+                                         head_dim=128, kv_dtype="fp8", src_dtype="bf16", seed=56, num_blocks=60),
+    "fp8_from_f32_d64": lambda: W.make_step("af8f", [40, 33, 16], [1] * 3, num_q_heads=4, num_kv_heads=2,
+                                            head_dim=64, q_dtype="f32", kv_dtype="fp8", src_dtype="f32", seed=57),
 }
 
 

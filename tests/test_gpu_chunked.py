@@ -28,13 +28,14 @@ def run_and_check(step, gpu):
     return cache
 
 
-def test_mixed_int8_prefill_full_size(gpu):
-    """4 chunks of 512 rows over a 1536-token prefix, int8 KV: every output."""
-    step = W.mixed_int8(num_decode=4)
+@pytest.mark.parametrize("kv", ["i8", "fp8"])
+def test_mixed_quantized_prefill_full_size(gpu, kv):
+    """4 chunks of 512 rows over a 1536-token prefix, int8 or fp8 KV: every output."""
+    step = W.mixed_int8(num_decode=4, kv_dtype=kv)
     run_and_check(step, gpu)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
 @pytest.mark.parametrize("lens", [
     ([64], [64]),                  # no prefix, one full tile
     ([200, 77, 1, 130], [70, 77, 1, 65]),  # ragged chunks and prefixes
@@ -94,7 +95,7 @@ def test_chunked_bad_metadata_gives_nan(gpu):
     assert O.compare(out[80:], ro[80:])["ok"]
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
 @pytest.mark.parametrize("Hq,Hkv", [(16, 8), (16, 4), (16, 2)])
 def test_multi_token_decode_rows(gpu, kv, Hq, Hkv):
     """The speculative-verification shape: 2..8 new rows per sequence over

@@ -36,7 +36,12 @@ def check(got, ref, what):
     lambda: W.make_step("q8f", [40, 33], [3, 1], num_q_heads=4, num_kv_heads=2, head_dim=64, q_dtype="f32",
                         kv_dtype="i8", src_dtype="f32", seed=42),
     lambda: W.make_step("bf64", [40, 33], [1, 1], num_q_heads=8, num_kv_heads=2, head_dim=64, seed=43),
-], ids=["tiny_f32", "qwen3_bf16", "int8_from_bf16", "int8_from_f32_d64", "bf16_d64"])
+    lambda: W.make_step("f8", [300, 77, 1, 16, 17], [300, 1, 1, 1, 5], num_q_heads=16, num_kv_heads=8,
+                        head_dim=128, kv_dtype="fp8", src_dtype="bf16", seed=44, num_blocks=40),
+    lambda: W.make_step("f8f", [40, 33], [3, 1], num_q_heads=4, num_kv_heads=2, head_dim=64, q_dtype="f32",
+                        kv_dtype="fp8", src_dtype="f32", seed=45),
+], ids=["tiny_f32", "qwen3_bf16", "int8_from_bf16", "int8_from_f32_d64", "bf16_d64", "fp8_from_bf16",
+        "fp8_from_f32_d64"])
 def test_reshape_and_cache_bytes_match_oracle(gpu, make):
     step = make()
     G.announce(f"reshape {step.name}")
@@ -139,12 +144,14 @@ def test_long_decode_full_size_sampled(gpu):
 
 
 @pytest.mark.parametrize("D,G_,kv,qd", [(64, 1, "bf16", "bf16"), (64, 4, "bf16", "f32"), (128, 8, "f32", "f32"),
-                                        (128, 4, "i8", "bf16"), (64, 2, "i8", "f32"), (128, 1, "bf16", "bf16")])
+                                        (128, 4, "i8", "bf16"), (64, 2, "i8", "f32"), (128, 1, "bf16", "bf16"),
+                                        (128, 2, "fp8", "bf16"), (64, 4, "fp8", "f32"), (128, 8, "fp8", "bf16")])
 def test_decode_shapes_and_dtypes(gpu, D, G_, kv, qd):
     Hkv = 2
+    scaled = kv in ("i8", "fp8")
     step = W.make_step(f"shape{D}_{G_}_{kv}", [1, 15, 16, 17, 100, 257], [1] * 6, num_q_heads=Hkv * G_,
                        num_kv_heads=Hkv, head_dim=D, q_dtype=qd, kv_dtype=kv,
-                       src_dtype=("bf16" if kv == "i8" and qd == "bf16" else ("f32" if kv == "i8" else kv)),
+                       src_dtype=(qd if scaled else kv),
                        num_splits=[1, 1, 2, 2, 3, 5], seed=50 + D + G_)
     cache = G.build_cache(step, gpu)
     out, lse = G.run_decode(step, cache, gpu)
@@ -153,8 +160,9 @@ def test_decode_shapes_and_dtypes(gpu, D, G_, kv, qd):
     check(lse, rl, "lse")
 
 
-def test_int8_decode_rows_of_mixed_step(gpu):
-    step = W.mixed_int8(num_prefill=1, num_decode=24, seed=1915)
+@pytest.mark.parametrize("kv", ["i8", "fp8"])
+def test_quantized_decode_rows_of_mixed_step(gpu, kv):
+    step = W.mixed_int8(num_prefill=1, num_decode=24, seed=1915, kv_dtype=kv)
     cache = G.build_cache(step, gpu)
     out, lse = G.run_decode(step, cache, gpu)
     ro, rl = O.decode(step, O.pool(step))
@@ -178,16 +186,16 @@ def test_every_split_count_agrees(gpu):
 # indexing: bit-exact probes
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("kv", ["bf16", "f32", "i8"])
+@pytest.mark.parametrize("kv", ["bf16", "f32", "i8", "fp8"])
 def test_one_hot_probe_returns_the_value_row_exactly(gpu, kv):
     """All keys zero except key j = alpha q, with the q heads of a group equal:
     every other weight underflows to exactly 0, so out == V_j bit for bit
-    (int8: code * scale in float32)."""
+    (int8 and fp8: value(code) * scale rounded once to float32)."""
     import torch
     n, Hq, Hkv, D = 45, 4, 2, 64
     qd = "f32" if kv == "f32" else "bf16"
     base = W.make_step("onehot", [n], [1], num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, q_dtype=qd,
-                       kv_dtype=kv, src_dtype=("bf16" if kv == "i8" else kv), seed=70, num_blocks=6)
+                       kv_dtype=kv, src_dtype=("bf16" if kv in ("i8", "fp8") else kv), seed=70, num_blocks=6)
     qv = np.zeros((1, Hq, D), np.float32)
     qv[0, :, :8] = 1.0                       # all heads equal; |q|^2 = 8
     q = qv if qd == "f32" else W.f32_to_bf16_bits(qv)

@@ -47,7 +47,7 @@ def decode_step(kv):
     return share_prefix(step, [(0, 1, 12), (0, 2, 8), (4, 3, 5)])
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
 @pytest.mark.parametrize("ns", [1, 3])
 def test_decode_over_shared_prefix_blocks(gpu, kv, ns):
     step = decode_step(kv)
@@ -75,7 +75,7 @@ def test_balanced_decode_over_shared_prefix_blocks(gpu):
     assert st["ok"], st
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
 def test_chunked_over_shared_prefix_blocks(gpu, kv):
     """Two chunks continue one cached prefix (the second request's prefix
     blocks are the first's), next to a decode row that shares them too."""
