@@ -76,14 +76,18 @@ WORKLOADS = {
     "mixed_int8_decode": (lambda W, seed, mts, batch, r: W.mixed_int8(seed=seed + 1000 * r,
                                                                        max_tokens_per_split=mts or 512),
                           1, 512, {"workload": "mixed_int8_step_decode_rows", "context_lens": "uniform[256,4096]"}),
+    "mixed_fp8_decode": (lambda W, seed, mts, batch, r: W.mixed_int8(seed=seed + 1000 * r, kv_dtype="fp8",
+                                                                      max_tokens_per_split=mts or 512),
+                         1, 512, {"workload": "mixed_fp8_step_decode_rows", "context_lens": "uniform[256,4096]"}),
 }
-DEFAULT_SEEDS = {"qwen3_decode": 1902, "ragged_decode": 1903, "long_decode": 1904, "mixed_int8_decode": 1905}
+DEFAULT_SEEDS = {"qwen3_decode": 1902, "ragged_decode": 1903, "long_decode": 1904, "mixed_int8_decode": 1905,
+                 "mixed_fp8_decode": 1905}
 # Decode mode measured fastest on MI355X per shape: one workgroup per
 # (split, kv head) for the Qwen3 step (one split per sequence), the uniform
 # long contexts and the int8 batch (512-token splits); the log-uniform ragged
 # batch gains from the balanced deal of tiles.
 DEFAULT_MODES = {"qwen3_decode": "splits", "ragged_decode": "balanced", "long_decode": "splits",
-                 "mixed_int8_decode": "splits"}
+                 "mixed_int8_decode": "splits", "mixed_fp8_decode": "splits"}
 
 
 def parse():
@@ -101,6 +105,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunked", action="store_true", help="skip the chunked-prefill MFMA measurement")
+    ap.add_argument("--chunked-kv", choices=("i8", "fp8"), default="i8",
+                    help="KV cache dtype of the mixed step in the chunked-prefill measurement")
     ap.add_argument("--no-fuse", action="store_true",
                     help="write the new rows with a separate reshape_and_cache launch instead of inside the decode")
     ap.add_argument("--seed", type=int, default=None)
@@ -158,7 +164,7 @@ class Replica:
                 return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-        code = {"f32": pkv.F32, "bf16": pkv.BF16, "i8": pkv.I8}
+        code = {"f32": pkv.F32, "bf16": pkv.BF16, "i8": pkv.I8, "fp8": pkv.FP8}
         self.cache = pkv.KVCache.allocate(step.num_blocks, step.num_kv_heads, step.head_dim, code[step.kv_dtype], dev)
         pkv.reshape_and_cache(dt(step.prefix_k, step.src_dtype), dt(step.prefix_v, step.src_dtype),
                               dt(step.prefix_slots.astype(np.int64), "i64"), self.cache)
@@ -185,7 +191,7 @@ class Replica:
             self.o_part = flat[: B * S * Hq * D].view(B, S, Hq, D)
             self.lse_part = flat[B * S * Hq * D: B * S * Hq * (D + 1)].view(B, S, Hq)
         self.tokens = int(ctx.sum())
-        eb, sb = {"f32": (4, 0), "bf16": (2, 0), "i8": (1, 4)}[step.kv_dtype]
+        eb, sb = {"f32": (4, 0), "bf16": (2, 0), "i8": (1, 4), "fp8": (1, 4)}[step.kv_dtype]
         self.kv_bytes = self.tokens * kv_bytes_per_token(step.num_kv_heads, step.head_dim, eb, sb)
         self.batch = B
         # the decode launch writes the new rows too (split mode)
@@ -282,23 +288,24 @@ def chunked_flops(step) -> int:
     return total * step.num_q_heads * 4 * step.head_dim
 
 
-def measure_chunked(dev, iters: int = 200):
-    """The mixed int8 step: 4 x 512-row causal chunks over a 1536-token cached
-    prefix plus 124 decode rows. Times the chunked (MFMA) pass alone, and the
-    whole step (cache write of 2172 rows, chunked pass, decode pass)."""
+def measure_chunked(dev, iters: int = 200, kv_dtype: str = "i8"):
+    """The mixed int8 (or fp8) step: 4 x 512-row causal chunks over a
+    1536-token cached prefix plus 124 decode rows. Times the chunked (MFMA)
+    pass alone, and the whole step (cache write of 2172 rows, chunked pass,
+    decode pass)."""
     import numpy as np
     import torch
 
     import paged_kv_attention_19_amd as pkv
     import workloads as W
-    step = W.mixed_int8()
+    step = W.mixed_int8(kv_dtype=kv_dtype)
 
     def dt(a, kind):
         if kind == "bf16":
             return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    cache = pkv.KVCache.allocate(step.num_blocks, 8, 128, pkv.I8, dev)
+    cache = pkv.KVCache.allocate(step.num_blocks, 8, 128, {"i8": pkv.I8, "fp8": pkv.FP8}[kv_dtype], dev)
     pkv.reshape_and_cache(dt(step.prefix_k, "bf16"), dt(step.prefix_v, "bf16"),
                           dt(step.prefix_slots.astype(np.int64), "i64"), cache)
     new_k, new_v = dt(step.new_k, "bf16"), dt(step.new_v, "bf16")
@@ -341,9 +348,10 @@ def measure_chunked(dev, iters: int = 200):
         res[name] = a.elapsed_time(b) / 1e3 / (max(1, iters // 20) * 20)
     flops = chunked_flops(step)
     tflops = flops / res["chunked"] / 1e12
+    kv_name = {"i8": "int8", "fp8": "fp8"}[kv_dtype]
     return {
-        "workload": "4 x 512-row causal chunks over 1536-token int8 prefixes (16q/8kv/128), "
-                    "plus 124 int8 decode rows in the whole step",
+        "workload": f"4 x 512-row causal chunks over 1536-token {kv_name} prefixes (16q/8kv/128), "
+                    f"plus 124 {kv_name} decode rows in the whole step",
         "kernel": "chunked_kernel",
         "chunked_us": round(res["chunked"] * 1e6, 3),
         "algorithmic_gflop": round(flops / 1e9, 3),
@@ -365,7 +373,7 @@ def cpu_baseline(step, seconds):
     oracle.reshape_and_cache(pool, step.new_k, step.new_v, step.src_dtype, step.new_slots)
     q, tables, ctx, _ = step.decode_batch()
     q64 = oracle.decode_rows(q, step.q_dtype)
-    eb, sb = {"f32": (4, 0), "bf16": (2, 0), "i8": (1, 4)}[step.kv_dtype]
+    eb, sb = {"f32": (4, 0), "bf16": (2, 0), "i8": (1, 4), "fp8": (1, 4)}[step.kv_dtype]
     per_tok = kv_bytes_per_token(step.num_kv_heads, step.head_dim, eb, sb)
     done_bytes = 0
     seqs = 0
@@ -484,7 +492,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "f32": "f32", "i8": "i8 kv / bf16 q"}[reps[0].step.kv_dtype],
+        "dtype": {"bf16": "bf16", "f32": "f32", "i8": "i8 kv / bf16 q",
+                  "fp8": "fp8 e4m3 kv / bf16 q"}[reps[0].step.kv_dtype],
         "data": "synthetic",
         "config": dict(cfg_text, **{
             "batch": reps[0].batch,
@@ -512,7 +521,7 @@ def main():
     line["copy_reference"] = copy_reference(int(partial_bytes))
     if not args.no_chunked:
         log("timing the chunked prefill ...")
-        line["chunked_prefill"] = measure_chunked(dev)
+        line["chunked_prefill"] = measure_chunked(dev, kv_dtype=args.chunked_kv)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         line["cpu_baseline"] = cpu_baseline(reps[0].step, args.cpu_seconds)
