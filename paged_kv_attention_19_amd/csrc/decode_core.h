@@ -222,6 +222,48 @@ struct WaveDecoder {
     }
   }
 
+  // Stream `count` blocks of kv head kh of one sequence through a ring of
+  // PD + 1 register tiles (PD blocks in flight while one is reduced). Block j
+  // of the stream starts at token tok0 + j * stride * 16 and its id is
+  // trow[j * stride]; t1 is the sequence's end (rows past it are masked).
+  // Ids are read 64 at a time, one per lane, before their blocks stream; with
+  // use_early the first 64 come from `early` (read by the caller beside q).
+  // Ids outside the pool set `bad`. Every tile, also past the stream's end, is
+  // issued by the same instructions (past the end with a zero-size
+  // descriptor), so the compiler's wait counts cover exactly the block being
+  // reduced.
+  template <int PD>
+  __device__ __forceinline__ void stream_blocks(const DecodeParams& p, int kh, const int32_t* trow, int stride,
+                                                int tok0, int count, int t1, bool use_early, int early, bool& bad) {
+    Tile ring[PD + 1];
+    for (int c0 = 0; c0 < count; c0 += kWave) {
+      const int cn = min(kWave, count - c0);
+      int v = 0;
+      if (use_early && c0 == 0) v = early;
+      else if (lane < cn) v = trow[static_cast<size_t>(c0 + lane) * stride];
+      const bool lane_bad = lane < cn && static_cast<unsigned>(v) >= static_cast<unsigned>(p.num_blocks);
+      bad = bad || wave_any(lane_bad);
+      const int ids = (lane < cn && !lane_bad) ? v : 0;
+      auto issue = [&](int it, Tile& t) {
+        int rows = 0, id = 0;
+        if (it < cn) {
+          rows = min(kBlock, t1 - (tok0 + (c0 + it) * stride * kBlock));
+          id = readlane(ids, it);
+        }
+        load_tile(p, id, kh, rows, t);
+      };
+#pragma unroll
+      for (int k = 0; k < PD; ++k) issue(k, ring[k]);
+      for (int it = 0; it < cn; it += PD + 1) {
+#pragma unroll
+        for (int k = 0; k <= PD; ++k) {
+          issue(it + k + PD, ring[(k + PD) % (PD + 1)]);
+          if (it + k < cn) process(ring[k], p.scale_log2);
+        }
+      }
+    }
+  }
+
   // Bring the token slots to the wavefront's common reference max M.
   __device__ __forceinline__ void slots_to_common_max(float (&M)[G]) {
 #pragma unroll

@@ -65,7 +65,6 @@ __device__ __forceinline__ void append_rows(const DecodeParams& p, int b, int kh
 template <int KV, int QT, int D, int G, int NW, int PD>
 __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p) {
   using WD = WaveDecoder<KV, QT, D, G>;
-  using Tile = typename WD::Tile;
   constexpr int LPT = WD::LPT, TPI = WD::TPI, CPL = WD::CPL, EPL = WD::EPL;
 
   // cross-slot merge through LDS when the (wave, slot) states fit in 64 KiB
@@ -138,48 +137,10 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
 
   wd.reset();
 
-  // ---- this wave's blocks (blocks w, w + NW, ... of the split), in chunks
-  //      of 64: lane j holds the id of the chunk's block j; ids outside the
-  //      pool poison the result ----
-  const int32_t* trow = p.tables + static_cast<size_t>(b) * p.max_blocks + blk_lo + w;
+  // ---- stream this wave's blocks: blocks w, w + NW, ... of the split ----
   bool bad = bad_n;
-  auto take_ids = [&](int v, int valid) -> int {
-    const bool lane_bad = lane < valid && static_cast<unsigned>(v) >= static_cast<unsigned>(p.num_blocks);
-    bad = bad || wave_any(lane_bad);
-    return (lane < valid && !lane_bad) ? v : 0;
-  };
-  Tile ring[PD + 1];
-  for (int c0 = 0; c0 < nb_w; c0 += kWave) {
-    const int cn = min(kWave, nb_w - c0);
-    int ids;
-    if (s == 0 && c0 == 0) {
-      ids = take_ids(early_ids, cn);   // blk_lo == 0: the early read holds them
-    } else {
-      const int j = c0 + lane;
-      ids = take_ids(lane < cn ? trow[static_cast<size_t>(j) * NW] : 0, cn);
-    }
-    // tile `it` of the chunk: its id and valid rows (0 past the chunk, so
-    // that the ring is filled by the same instructions every time)
-    auto issue = [&](int it, Tile& t) {
-      int rows = 0, id = 0;
-      if (it < cn) {
-        rows = min(kBlock, t1 - (t0 + (w + (c0 + it) * NW) * kBlock));
-        id = readlane(ids, it);
-      }
-      wd.load_tile(p, id, kh, rows, t);
-    };
-    // ---- stream the chunk with PD tiles of K/V in flight ahead: a ring of
-    //      PD + 1 register tiles, indexed statically (fully unrolled) ----
-#pragma unroll
-    for (int k = 0; k < PD; ++k) issue(k, ring[k]);
-    for (int it = 0; it < cn; it += PD + 1) {
-#pragma unroll
-      for (int k = 0; k <= PD; ++k) {
-        issue(it + k + PD, ring[(k + PD) % (PD + 1)]);
-        if (it + k < cn) wd.process(ring[k], p.scale_log2);
-      }
-    }
-  }
+  wd.template stream_blocks<PD>(p, kh, p.tables + static_cast<size_t>(b) * p.max_blocks + blk_lo + w, NW,
+                                t0 + w * kBlock, nb_w, t1, s == 0, early_ids, bad);
 
   // ---- merge: bring the wave's token slots to one reference max ----
   float M[G];
@@ -312,7 +273,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
     const int nb = bb < p.batch ? blocks_of(p.ctx[bb], p.max_blocks) : 0;
     T += wave_sum_i32(nb);
   }
-  T *= Hkv;
+  T = uniform64(T) * Hkv;   // the same on every lane: scalar registers
 
   // ---- sequences without tiles: n == 0 -> (0, -inf); bad n -> NaN ----
   for (int bb = gw; bb < p.batch; bb += nw_grid) {
@@ -352,8 +313,11 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
     }
     base += total;
   }
+  // the cursors are the same on every lane: keep them in scalar registers,
+  // so the tile addresses built from them (buffer descriptors) are uniform
   b = __builtin_amdgcn_readfirstlane(b);
-  int n = p.ctx[b];
+  base = uniform64(base);
+  int n = __builtin_amdgcn_readfirstlane(p.ctx[b]);
   int nb = blocks_of(n, p.max_blocks);
   if (nb == 0) return;   // cannot happen for r0 < T; keeps the divisions below safe
   int kh = static_cast<int>((r0 - base) / nb);
@@ -370,7 +334,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
     cbase += static_cast<int64_t>(Hkv) * cnb;
     do {
       ++cb;
-      cn = cb < p.batch ? p.ctx[cb] : kBlock;
+      cn = cb < p.batch ? __builtin_amdgcn_readfirstlane(p.ctx[cb]) : kBlock;
       cnb = blocks_of(cn, p.max_blocks);
     } while (cnb == 0);
   };
