@@ -51,6 +51,53 @@ def test_reshape_and_cache_bytes_match_oracle(gpu, make):
         assert got[name] == ref[name], name
 
 
+def _quantizer_edge_rows(kv: str, T: int, H: int, D: int, seed: int) -> np.ndarray:
+    """float32 rows [T][H][D] whose first element sets amax so that the scale is
+    a power of two s exactly (amax = 127 s or 448 s), the rest placed at the
+    quantizer's hard cases times s: for int8 the quotients k + 1/2 and a few
+    ulps either side; for fp8 the midpoints between neighbouring E4M3 values,
+    their float32 neighbours, and the subnormal range below 2^-6."""
+    rng = np.random.default_rng(seed)
+    top = 127.0 if kv == "i8" else 448.0
+    if kv == "i8":
+        k = np.arange(-127, 127, dtype=np.float64)
+        hard = np.float32(k + 0.5)
+    else:
+        pos = O.oracle.fp8_e4m3_value(np.arange(0x7F))
+        hard = np.float32((pos[:-1] + pos[1:]) / 2)
+        hard = np.concatenate([hard, np.float32(rng.uniform(0, 2.0 ** -6, 200))])
+    hard = np.concatenate([hard, np.nextafter(hard, np.float32(0)), np.nextafter(hard, np.float32(1e9))])
+    hard = np.concatenate([hard, -hard]).astype(np.float32)
+    rows = np.empty((T, H, D), np.float32)
+    for t in range(T):
+        for h in range(H):
+            e = int(rng.integers(-6, 7))
+            sc = np.float32(2.0 ** e)
+            rows[t, h, 0] = np.float32(top) * sc * (1 if rng.random() < 0.5 else -1)
+            rows[t, h, 1:] = rng.choice(hard, D - 1) * sc
+    return rows
+
+
+@pytest.mark.parametrize("kv", ["i8", "fp8"])
+def test_quantizer_hard_cases_bit_exact(gpu, kv):
+    """Quotients on and next to the rounding boundaries (and, for fp8, in the
+    subnormal range): the cache bytes must equal the oracle's."""
+    import torch
+    T, H, D = 64, 2, 64
+    K = _quantizer_edge_rows(kv, T, H, D, 7)
+    V = _quantizer_edge_rows(kv, T, H, D, 8)
+    slots = np.random.default_rng(9).permutation(4 * 16)[:T].astype(np.int64)
+    cache = G.pkv.KVCache.allocate(4, H, D, G.CODE[kv], gpu)
+    G.announce(f"reshape hard cases {kv}")
+    G.pkv.reshape_and_cache(G.tensor(K, "f32", gpu), G.tensor(V, "f32", gpu), G.ints(slots, gpu, torch.int64), cache)
+    torch.cuda.synchronize()
+    p = O.oracle.OraclePool(4, H, 16, D, kv)
+    O.oracle.reshape_and_cache(p, K, V, "f32", slots)
+    got, ref = G.cache_bytes(cache), O.pool_bytes(p)
+    for name in ref:
+        assert got[name] == ref[name], name
+
+
 def test_reshape_skips_negative_and_out_of_range_slots(gpu):
     import torch
     step = W.make_step("skip", [20], [20], num_q_heads=4, num_kv_heads=2, head_dim=64, seed=44, num_blocks=4)
