@@ -43,7 +43,10 @@ def check(step, gpu):
     lambda: W.mixed_int8(num_prefill=1, num_decode=24, seed=1915),
     lambda: W.make_step("b64", [1, 15, 16, 17, 100, 257], [1] * 6, num_q_heads=8, num_kv_heads=2, head_dim=64,
                         q_dtype="f32", kv_dtype="f32", seed=140),
-], ids=["tiny", "qwen3", "qwen3_b5", "ragged24", "int8_rows", "f32_d64"])
+    lambda: W.mixed_int8(num_prefill=1, num_decode=24, seed=1915, kv_dtype="fp8"),
+    lambda: W.make_step("b64f8", [1, 15, 16, 17, 100, 257], [1] * 6, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                        q_dtype="f32", kv_dtype="fp8", src_dtype="f32", seed=141),
+], ids=["tiny", "qwen3", "qwen3_b5", "ragged24", "int8_rows", "f32_d64", "fp8_rows", "fp8_d64_f32q"])
 def test_balanced_matches_oracle(gpu, make):
     check(make(), gpu)
 
