@@ -20,12 +20,15 @@
 //                 registers): every lane holds scores of ONE query row, so the
 //                 row max, the causal mask and the softmax state are lane-local
 //                 (the two lanes l, l^32 of a row hold its two token quarters);
-//   O^T = V^T P^T (A = V^T from LDS, B = P^T straight from the S^T registers,
-//                 as a bf16 high part plus a bf16 residual, two MFMAs: one
-//                 bf16 rounding of a weight (2^-9) is too coarse for rows that
-//                 see few keys, the pair keeps ~2^-17): the output accumulator
-//                 again holds one query row per lane, so the online rescale is
-//                 lane-local.
+//   O^T = V^T P^T (A = V^T from LDS, B = P^T straight from the S^T registers):
+//                 the output accumulator again holds one query row per lane,
+//                 so the online rescale is lane-local. A bf16 cache runs it
+//                 twice, on a bf16 high part of P and on its bf16 residual:
+//                 one bf16 rounding of a weight (2^-9) is too coarse for rows
+//                 that see few keys, the pair keeps ~2^-17. An int8 or fp8
+//                 cache stages V as fp16 instead (its codes are exact there)
+//                 and runs it once on P rounded to fp16 (2^-12), with the V
+//                 scale folded into P.
 // K rows are fed to the first product in an order that swaps bits 2 and 3 of
 // the row index; with it, the token order of the S^T registers is exactly the
 // k order the second product needs, so P never moves between lanes.
@@ -41,8 +44,8 @@
 // and blocks outside the table come back as zeros with no branch, so every
 // tile issues the same loads and only the older set is waited for. An int8
 // or fp8 cache is dequantized on its way to LDS (int8 codes and E4M3 values
-// are exact in bf16): the K scale multiplies the score column, the V scale
-// the weight.
+// are exact in bf16 and in fp16; K goes to bf16 beside the bf16 q rows, V to
+// fp16): the K scale multiplies the score column, the V scale the weight.
 #include <type_traits>
 #include <utility>
 
@@ -54,6 +57,8 @@ namespace pkv {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
@@ -82,6 +87,24 @@ __device__ __forceinline__ int vt_off(int d, int u) { return d * 128 + ((u ^ vt_
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// two floats -> fp16 pair, each rounded to nearest even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  f16x2_t v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Byte B of two int8 code words -> fp16 pair (low half from w0), exact: the
+// code c, offset to u = c + 128 by flipping its sign bit, becomes the low
+// byte of the fp16 number 1024 + u (the numbers 1024 .. 2047 are spaced by
+// 1), and subtracting 1152 leaves c.
+template <int B>
+__device__ __forceinline__ uint32_t i8pair_to_f16x2(uint32_t w0, uint32_t w1) {
+  constexpr uint32_t sel = 0x0c000c00u | ((4u + B) << 16) | static_cast<uint32_t>(B);
+  const uint32_t x = __builtin_amdgcn_perm(w1, w0, sel) ^ 0x64806480u;
+  const f16x2_t v = __builtin_bit_cast(f16x2_t, x) - f16x2_t{static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
   return __builtin_bit_cast(uint32_t, v);
 }
 
@@ -128,10 +151,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   constexpr int P = kRows / G;               // positions per query tile
   constexpr bool kScaled = is_scaled_kv(KV);   // int8 / fp8 codes + a scale per row
   constexpr float kSlack = 8.0f;
+  // 8-bit caches: the fp16 weights are exp2(score - m - kP16Shift - lvs) x
+  // V scale, where 2^lvs is a power of two at least twice every V scale the
+  // workgroup reads (found once, before the loop). So they stay below
+  // 2^(kSlack - kP16Shift - 1) = 8 whatever the magnitude of V, and the
+  // weights that matter stay clear of fp16's subnormal range.
+  constexpr float kP16Shift = 4.0f;
   constexpr int kRowBytes = kScaled ? kD : 2 * kD;   // bytes of one cached K or V row
   constexpr int kUnit = kRowBytes / 16;          // bytes of 8 dims of a cached row
   __shared__ __attribute__((aligned(16))) char s_kv[kStages][kStageBytes];
   __shared__ __attribute__((aligned(16))) float s_sc[kStages][2 * kTile];   // 8-bit codes: K scale x softmax scale, V scale
+  __shared__ float s_vmax[kThreads / 64];   // 8-bit codes: largest V scale each wavefront saw
   __shared__ __attribute__((aligned(16))) int s_ids[kIdsCached];
   static_assert(kStages * kStageBytes >= 4 * kMergeFloats * 64 * 4, "merge area");
 
@@ -311,16 +341,23 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       return st.k[i];
     }
   };
-  // the two V tokens of st as bf16 words: vw[i][k] = dims 8 u + 2k, +1 of token 2 tg + i
-  auto v_bf16 = [&](const Staged& st, uint32_t (&vw)[2][4]) {
+  // the two V tokens of st as 16-bit words (bf16 for a bf16 cache, fp16 for
+  // fp8 codes): vw[i][k] = dims 8 u + 2k, +1 of token 2 tg + i. int8 codes
+  // need no step here: v_word converts them straight from st.
+  auto v_prep = [&](const Staged& st, uint32_t (&vw)[2][4]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if constexpr (kScaled) {
-        vw[i][0] = code_pair_to_bf16x2<KV, 0>(st.v[i].x);
-        vw[i][1] = code_pair_to_bf16x2<KV, 2>(st.v[i].x);
-        vw[i][2] = code_pair_to_bf16x2<KV, 0>(st.v[i].y);
-        vw[i][3] = code_pair_to_bf16x2<KV, 2>(st.v[i].y);
-      } else {
+      if constexpr (KV == PKV_FP8) {
+        // exact: E4M3 values are fp16 values
+        const f32x2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(st.v[i].x), false);
+        const f32x2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(st.v[i].x), true);
+        const f32x2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(st.v[i].y), false);
+        const f32x2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(st.v[i].y), true);
+        vw[i][0] = pack_f16(f0.x, f0.y);
+        vw[i][1] = pack_f16(f1.x, f1.y);
+        vw[i][2] = pack_f16(f2.x, f2.y);
+        vw[i][3] = pack_f16(f3.x, f3.y);
+      } else if constexpr (KV == PKV_BF16) {
         vw[i][0] = st.v[i].x;
         vw[i][1] = st.v[i].y;
         vw[i][2] = st.v[i].z;
@@ -328,9 +365,20 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       }
     }
   };
-  // dim 8 u + e of the two tokens, packed
-  auto v_pair = [&](const uint32_t (&vw)[2][4], int e) -> uint32_t {
-    return __builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+  // dim 8 u + e of the two tokens as one word of the V^T stage (token 2 tg low)
+  auto v_word = [&](const Staged& st, const uint32_t (&vw)[2][4], int e) -> uint32_t {
+    if constexpr (KV == PKV_I8) {
+      const uint32_t w0 = (e < 4) ? st.v[0].x : st.v[0].y;
+      const uint32_t w1 = (e < 4) ? st.v[1].x : st.v[1].y;
+      switch (e & 3) {
+        case 0: return i8pair_to_f16x2<0>(w0, w1);
+        case 1: return i8pair_to_f16x2<1>(w0, w1);
+        case 2: return i8pair_to_f16x2<2>(w0, w1);
+        default: return i8pair_to_f16x2<3>(w0, w1);
+      }
+    } else {
+      return __builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+    }
   };
   auto sc_store = [&](const Staged& st, int stage) {
     if constexpr (kScaled) {
@@ -344,9 +392,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(sb + kw_off + 4096 * i) = k_bf16(st, i);
     uint32_t vw[2][4];
-    v_bf16(st, vw);
+    v_prep(st, vw);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(sb + vw_off(e)) = v_pair(vw, e);
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(sb + vw_off(e)) = v_word(st, vw, e);
     sc_store(st, stage);
   };
 
@@ -375,11 +423,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 
   // ---- online softmax state of this lane's row, over this wavefront's tokens ----
   float m = neg_inf(), l = 0.f;
+  float mu_off = 0.f;   // 8-bit caches: kP16Shift + lvs, set before the loop
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
   f32x16_t sacc;   // S^T of the tile being softmaxed
-  bf16x8_t phi[2], plo[2];   // P^T of that tile: bf16 high parts and residuals
+  bf16x8_t phi[2], plo[2];   // P^T of that tile: bf16 high parts and residuals (8-bit caches: fp16 in phi)
 
   // scores: register v of the wavefront's half holds token
   // 32 th + 8 h + 16 (v / 8) + (v % 8) of the tile; chunk c = v / 4
@@ -446,7 +495,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
         corr = need ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;   // m = -inf -> 0
         l *= corr;
         m = need ? tmax : m;
-        mu = (m == neg_inf()) ? 0.f : m;
+        mu = (m == neg_inf()) ? 0.f : (kScaled ? m + mu_off : m);
       }
       float vv[4];
       if constexpr (kScaled) {
@@ -464,11 +513,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
           rsum += pw[k];
           if constexpr (kScaled) pw[k] *= vv[e + k];
         }
-        // high parts rounded to bf16, residuals exact in float32 then rounded
-        const uint32_t hp = pack_bf16(pw[0], pw[1]);
-        const uint32_t lp = pack_bf16(pw[0] - __uint_as_float(hp << 16), pw[1] - __uint_as_float(hp & 0xffff0000u));
-        pw_hi[v >> 1] = hp;
-        pw_lo[v >> 1] = lp;
+        if constexpr (kScaled) {
+          pw_hi[v >> 1] = pack_f16(pw[0], pw[1]);
+        } else {
+          // high parts rounded to bf16, residuals exact in float32 then rounded
+          const uint32_t hp = pack_bf16(pw[0], pw[1]);
+          const uint32_t lp = pack_bf16(pw[0] - __uint_as_float(hp << 16), pw[1] - __uint_as_float(hp & 0xffff0000u));
+          pw_hi[v >> 1] = hp;
+          pw_lo[v >> 1] = lp;
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -477,7 +530,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       phi[k2] = __builtin_bit_cast(bf16x8_t, make_uint4(pw_hi[4 * k2], pw_hi[4 * k2 + 1], pw_hi[4 * k2 + 2], pw_hi[4 * k2 + 3]));
-      plo[k2] = __builtin_bit_cast(bf16x8_t, make_uint4(pw_lo[4 * k2], pw_lo[4 * k2 + 1], pw_lo[4 * k2 + 2], pw_lo[4 * k2 + 3]));
+      if constexpr (!kScaled) {
+        plo[k2] = __builtin_bit_cast(bf16x8_t, make_uint4(pw_lo[4 * k2], pw_lo[4 * k2 + 1], pw_lo[4 * k2 + 2], pw_lo[4 * k2 + 3]));
+      }
     }
     if (wave_any(corr != 1.f)) {
 #pragma unroll
@@ -489,7 +544,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   // Phase 2 of tile j: O^T += V_j^T P_j^T over this wavefront's 32 tokens
   // (V in stage sv_stage) || this group's half of tile j + 2 from st to
   // stage st_stage, then tile j + 3's loads (from ns) into st; 8 slots of two
-  // MFMAs on different accumulators.
+  // bf16 MFMAs (8-bit caches: one fp16 MFMA) on different accumulators.
   auto phase2 = [&](int j, int sv_stage, int st_stage, Staged& st, const TileSrc& ns) {
     const char* vb = s_kv[sv_stage];
     char* wb = s_kv[st_stage];
@@ -497,8 +552,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) va[0][db] = lds_read16(vb + vr_off[db][0]);
     uint32_t vw[2][4];
-    // slot s: k-step k2 = s / 4; (s % 4) = high part of dims blocks 0,1 / 2,3,
-    // then the residual of 0,1 / 2,3
+    // slot s: k-step k2 = s / 4. A bf16 cache: (s % 4) = high part of dims
+    // blocks 0,1 / 2,3, then the residual of 0,1 / 2,3. 8-bit caches: one
+    // fp16 MFMA on dims block s % 4.
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
       const int k2 = sl >> 2, q = sl & 3;
@@ -506,22 +562,27 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) va[1][db] = lds_read16(vb + vr_off[db][1]);
       }
-      const bf16x8_t b = (q < 2) ? phi[k2] : plo[k2];
+      if constexpr (kScaled) {
+        o[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, va[k2][q]),
+                                                      __builtin_bit_cast(f16x8_t, phi[k2]), o[q], 0, 0, 0);
+      } else {
+        const bf16x8_t b = (q < 2) ? phi[k2] : plo[k2];
 #pragma unroll
-      for (int d2 = 0; d2 < 2; ++d2) {
-        const int db = 2 * (q & 1) + d2;
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va[k2][db]), b, o[db], 0, 0, 0);
+        for (int d2 = 0; d2 < 2; ++d2) {
+          const int db = 2 * (q & 1) + d2;
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va[k2][db]), b, o[db], 0, 0, 0);
+        }
       }
       // staging of tile j + 2 (st -> LDS stage st_stage), then tile j + 3's loads
       if (sl < 2) {
         *reinterpret_cast<uint4*>(wb + kw_off + 4096 * sl) = k_bf16(st, sl);
       } else if (sl == 2) {
-        v_bf16(st, vw);
+        v_prep(st, vw);
       } else if (sl < 7) {
 #pragma unroll
         for (int e2 = 0; e2 < 2; ++e2) {
           const int e = 2 * (sl - 3) + e2;
-          *reinterpret_cast<uint32_t*>(wb + vw_off(e)) = v_pair(vw, e);
+          *reinterpret_cast<uint32_t*>(wb + vw_off(e)) = v_word(st, vw, e);
         }
       } else {
         sc_store(st, st_stage);
@@ -532,17 +593,40 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   };
 
   // ---- prologue: this group's halves of tiles 0 and 1 in LDS, tile 2 in
-  // flight, S^T of tile 0 ----
+  // flight, S^T of tile 0; 8-bit caches: the largest V scale of keys
+  // [0, kv_end), each thread scanning every 512th key ----
   Staged sa{};
+  float vmax = 0.f;
   {
     Staged sb{};
     gload(0, sa);
     gload(1, sb);
+    if constexpr (kScaled) {
+      for (int t = tid; t < kv_end; t += kThreads) {
+        const int blk = t / kBlock;
+        const int id = blk < kIdsCached ? s_ids[blk] : trow[blk];
+        if (static_cast<unsigned>(id) < static_cast<unsigned>(p.num_blocks)) {
+          vmax = fmaxf(vmax, p.v_scale[(static_cast<size_t>(id) * p.num_kv_heads + kh) * kBlock + t % kBlock]);
+        }
+      }
+    }
     lstore(sa, 0);
     lstore(sb, 1);
   }
   gload(2, sa);
+  if constexpr (kScaled) {
+#pragma unroll
+    for (int x = 1; x < 64; x <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, x));   // NaN ignored
+    if (lane == 0) s_vmax[w] = vmax;
+  }
   __syncthreads();
+  // 8-bit caches: 2^lvs >= twice every V scale read (lvs = 0 if all are 0)
+  if constexpr (kScaled) {
+    float vm = s_vmax[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) vm = fmaxf(vm, s_vmax[i]);
+    mu_off = kP16Shift + (vm > 0.f ? static_cast<float>(__builtin_amdgcn_frexp_expf(vm) + 1) : 0.f);
+  }
   qk(0, sacc);
 
   // ---- main loop. Every wavefront runs phase 1 and phase 2 of each tile
@@ -574,6 +658,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 
   // ---- merge the two token halves: wavefront w + 4 hands (o, m, l) to w ----
   bad = __syncthreads_or(bad);   // also: every wavefront is done with the stages
+  // the exponent o and l are taken relative to (8-bit caches: with the V scale reference)
+  const float mref = (kScaled && m != neg_inf()) ? m + mu_off : m;
   float* mb = reinterpret_cast<float*>(&s_kv[0][0]) + (rb * kMergeFloats) * 64 + lane;   // [rb][66][64 lanes]
   if (th == 1) {
 #pragma unroll
@@ -581,14 +667,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) mb[(16 * db + v) * 64] = o[db][v];
     }
-    mb[64 * 64] = m;
+    mb[64 * 64] = mref;
     mb[65 * 64] = l;
   }
   __syncthreads();
   if (th == 1 || !row_live) return;
   const float m2 = mb[64 * 64], l2 = mb[65 * 64];
-  const float mm = fmaxf(m, m2);
-  const float a1 = (m == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+  const float mm = fmaxf(mref, m2);
+  const float a1 = (mref == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mref - mm);
   const float a2 = (m2 == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
   const float lt = l * a1 + l2 * a2;
   const float inv = norm_inv(lt);

@@ -13,17 +13,18 @@ from tests import oracle_side as O
 pytestmark = pytest.mark.gpu
 
 
-def check(got, ref, what):
-    st = O.compare(got, ref)
+def check(got, ref, what, atol=O.ATOL):
+    st = O.compare(got, ref, atol=atol)
+    print(f"{what}: max_abs {st['max_abs']:.3g} max_rel {st['max_rel']:.3g} over {st['n']}")
     assert st["ok"], f"{what}: {st}"
     return st
 
 
-def run_and_check(step, gpu):
+def run_and_check(step, gpu, out_atol=O.ATOL):
     cache = G.build_cache(step, gpu)
     out, lse = G.run_chunked(step, cache, gpu)
     ro, rl = O.chunked(step, O.pool(step))
-    check(out, ro, "out")
+    check(out, ro, "out", out_atol)
     check(lse, rl, "lse")
     return cache
 
@@ -48,11 +49,34 @@ def test_chunked_shapes(gpu, kv, lens):
     run_and_check(step, gpu)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2), (16, 4), (16, 2)])
-def test_chunked_group_sizes(gpu, Hq, Hkv):
-    step = W.make_step(f"grp{Hq}_{Hkv}", [150, 96], [100, 40], num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,
-                       kv_dtype="bf16", seed=90 + Hq)
+def test_chunked_group_sizes(gpu, kv, Hq, Hkv):
+    step = W.make_step(f"grp{Hq}_{Hkv}_{kv}", [150, 96], [100, 40], num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,
+                       kv_dtype=kv, seed=90 + Hq)
     run_and_check(step, gpu)
+
+
+def _scale_bf16(bits: np.ndarray, log2: int) -> np.ndarray:
+    """bf16 values times 2^log2 (exact for these magnitudes)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** log2)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kv", ["i8", "fp8"])
+@pytest.mark.parametrize("log2", [-12, 12])
+def test_chunked_quantized_value_magnitudes(gpu, kv, log2):
+    """8-bit caches weight V in fp16 with the V scale folded into the weight:
+    V values 2^12 times larger (V scales ~130 for int8) stay finite, and 2^12
+    times smaller ones put the weights in fp16's subnormal range. The
+    absolute bound scales with |V| (any weighting's rounding error does); the
+    lse, which does not depend on V, keeps the plain bound. Chunks with no
+    prefix give rows that see 1, 2, 3 ... keys."""
+    import dataclasses
+    step = W.make_step(f"mag_{kv}_{log2}", [64, 300, 90], [64, 120, 90], num_q_heads=16, num_kv_heads=8,
+                       head_dim=128, kv_dtype=kv, src_dtype="bf16", seed=97)
+    step = dataclasses.replace(step, prefix_v=_scale_bf16(step.prefix_v, log2), new_v=_scale_bf16(step.new_v, log2))
+    run_and_check(step, gpu, out_atol=O.ATOL * 2.0 ** max(log2, 0))
 
 
 def test_chunk_rows_match_decode_at_their_positions(gpu):
