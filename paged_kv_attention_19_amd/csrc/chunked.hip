@@ -71,7 +71,7 @@ constexpr int kXcdsC = 8;
 constexpr int kStages = 3;
 constexpr int kKBytes = kTile * kD * 2;    // 16 KiB, row-major [token][dim], swizzled
 constexpr int kVBytes = kD * kTile * 2;    // 16 KiB, transposed [dim][token], swizzled
-constexpr int kStageBytes = kKBytes + kVBytes;
+static_assert(kKBytes == kVBytes, "K and V^T stages of one size");
 constexpr int kIdsCached = 4096;           // block ids kept in LDS (65536 tokens)
 constexpr int kRsrcWord3 = 0x00020000;     // buffer descriptor word 3 (gfx9 family): raw dwords
 constexpr int kMergeFloats = 66;           // per lane of a merging wavefront: o[64], m, l
@@ -134,7 +134,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int byt
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, kRsrcWord3);
 }
 
-__device__ __forceinline__ uint4 lds_read16(const char* a) { return *reinterpret_cast<const uint4*>(a); }
+typedef __attribute__((address_space(3))) char lds_char;
+
+// LDS byte address of a shared-memory location
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char*)p));
+}
+// A lane's LDS address, opaque to the compiler: accesses at it plus a
+// compile-time stage offset (< 64 KiB) keep that offset in the instruction's
+// immediate field, whatever the ring's own base, rather than adding it per
+// lane or holding one more register per stage.
+__device__ __forceinline__ uint32_t lane_address(uint32_t a) {
+  asm volatile("" : "+v"(a));
+  return a;
+}
+__device__ __forceinline__ uint4 lds_read16(uint32_t a, int off) {
+  const u32x4v_t x = *reinterpret_cast<const __attribute__((address_space(3))) u32x4v_t*>((const lds_char*)(uintptr_t)a + off);
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ void lds_write16(uint32_t a, int off, uint4 x) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4v_t*>((lds_char*)(uintptr_t)a + off) = u32x4v_t{x.x, x.y, x.z, x.w};
+}
+__device__ __forceinline__ void lds_write4(uint32_t a, int off, uint32_t x) {
+  *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>((lds_char*)(uintptr_t)a + off) = x;
+}
 
 // One tile's global loads for one thread, held in registers until they are
 // stored to LDS. A thread stages part of its group's 32-token half of the
@@ -159,11 +182,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   constexpr float kP16Shift = 4.0f;
   constexpr int kRowBytes = kScaled ? kD : 2 * kD;   // bytes of one cached K or V row
   constexpr int kUnit = kRowBytes / 16;          // bytes of 8 dims of a cached row
-  __shared__ __attribute__((aligned(16))) char s_kv[kStages][kStageBytes];
+  // stages 0 .. 2: K (row-major); stages 3 .. 5: V^T of the same tiles
+  __shared__ __attribute__((aligned(16))) char s_kv[2 * kStages][kKBytes];
   __shared__ __attribute__((aligned(16))) float s_sc[kStages][2 * kTile];   // 8-bit codes: K scale x softmax scale, V scale
   __shared__ float s_vmax[kThreads / 64];   // 8-bit codes: largest V scale each wavefront saw
   __shared__ __attribute__((aligned(16))) int s_ids[kIdsCached];
-  static_assert(kStages * kStageBytes >= 4 * kMergeFloats * 64 * 4, "merge area");
+  static_assert(2 * kStages * kKBytes >= 4 * kMergeFloats * 64 * 4, "merge area");
 
   // ---- work item: (sequence, kv head, query tile), XCD-contiguous ----
   const int QT = (p.max_q_len + P - 1) / P;
@@ -328,9 +352,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   };
 
   // LDS byte offsets of this thread's stores, the same for every stage
-  const int kw_off = k_off(32 * th + tg, u16);       // K chunk i: token 32 th + tg + 16 i, + 4096 i
+  const uint32_t k_lds = lds_address(&s_kv[0][0]), v_lds = lds_address(&s_kv[kStages][0]);
+  const uint32_t kw_a = lane_address(k_lds + k_off(32 * th + tg, u16));   // K chunk i: token 32 th + tg + 16 i, + 4096 i
   // V^T: dims 8 u + e, tokens 32 th + 2 tg, + 1 (4 bytes in unit 4 th + tg / 4)
-  auto vw_off = [&](int e) { return kKBytes + vt_off(8 * u16 + e, 4 * th + (tg >> 2)) + ((tg & 3) << 2); };
+  uint32_t vw_a[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vw_a[e] = lane_address(v_lds + vt_off(8 * u16 + e, 4 * th + (tg >> 2)) + ((tg & 3) << 2));
 
   // K chunk i of st -> bf16 (8-bit codes converted)
   auto k_bf16 = [&](const Staged& st, int i) -> uint4 {
@@ -388,35 +415,35 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     }
   };
   auto lstore = [&](const Staged& st, int stage) {
-    char* sb = s_kv[stage];
+    const int so = stage * kKBytes;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(sb + kw_off + 4096 * i) = k_bf16(st, i);
+    for (int i = 0; i < 2; ++i) lds_write16(kw_a, so + 4096 * i, k_bf16(st, i));
     uint32_t vw[2][4];
     v_prep(st, vw);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(sb + vw_off(e)) = v_word(st, vw, e);
+    for (int e = 0; e < 8; ++e) lds_write4(vw_a[e], so, v_word(st, vw, e));
     sc_store(st, stage);
   };
 
   // LDS byte offsets of this lane's MFMA operand reads, the same for every stage
   const int ar = lane & 31;
-  int kr_off[8];                                    // K row 32 th + sigma(ar), unit 2 ks + h
+  uint32_t kr_a[8];                                 // K row 32 th + sigma(ar), unit 2 ks + h
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) kr_off[ks] = k_off(32 * th + sigma(ar), 2 * ks + h);
-  int vr_off[4][2];                                 // V^T row 32 db + ar, unit 2 (2 th + k2) + h
+  for (int ks = 0; ks < 8; ++ks) kr_a[ks] = lane_address(k_lds + k_off(32 * th + sigma(ar), 2 * ks + h));
+  uint32_t vr_a[4][2];                              // V^T row 32 db + ar, unit 2 (2 th + k2) + h
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) vr_off[db][k2] = kKBytes + vt_off(32 * db + ar, 2 * (2 * th + k2) + h);
+    for (int k2 = 0; k2 < 2; ++k2) vr_a[db][k2] = lane_address(v_lds + vt_off(32 * db + ar, 2 * (2 * th + k2) + h));
   }
 
   // S^T of this wavefront's half of the tile in `stage`
   auto qk = [&](int stage, f32x16_t& s) {
-    const char* kb = s_kv[stage];
+    const int so = stage * kKBytes;
     s = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const uint4 a = lds_read16(kb + kr_off[ks]);
+      const uint4 a = lds_read16(kr_a[ks], so);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qb[ks], s, 0, 0, 0);
     }
   };
@@ -439,13 +466,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   // rescaled if the reference max moved and sacc becomes tile j + 1's S^T.
   auto phase1 = [&](auto diag_tag, int j, int sk, int ss) {
     constexpr bool kDiag = decltype(diag_tag)::value;
-    const char* kb = s_kv[sk];
+    const int so = sk * kKBytes;
     const float* scs = s_sc[ss];
     const int tlim = pos - j * kTile;     // tile tokens past this one are masked
     uint4 ka[3];
-    ka[0] = lds_read16(kb + kr_off[0]);
-    ka[1] = lds_read16(kb + kr_off[1]);
-    ka[2] = lds_read16(kb + kr_off[2]);
+    ka[0] = lds_read16(kr_a[0], so);
+    ka[1] = lds_read16(kr_a[1], so);
+    ka[2] = lds_read16(kr_a[2], so);
     float4 sc4;
     auto read_sc = [&](int t0) { sc4 = *reinterpret_cast<const float4*>(scs + t0); };
     if constexpr (kScaled) read_sc(tok_of(0));
@@ -455,7 +482,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     f32x16_t sn = f32x16_t{};
     auto mfma1 = [&](int ks) {
       sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks % 3]), qb[ks], sn, 0, 0, 0);
-      if (ks + 3 < 8) ka[ks % 3] = lds_read16(kb + kr_off[ks + 3]);
+      if (ks + 3 < 8) ka[ks % 3] = lds_read16(kr_a[ks + 3], so);
     };
     // slots 0-3: scale, mask and max of scores 4 c .. 4 c + 3
     float cmax = neg_inf();
@@ -546,11 +573,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   // stage st_stage, then tile j + 3's loads (from ns) into st; 8 slots of two
   // bf16 MFMAs (8-bit caches: one fp16 MFMA) on different accumulators.
   auto phase2 = [&](int j, int sv_stage, int st_stage, Staged& st, const TileSrc& ns) {
-    const char* vb = s_kv[sv_stage];
-    char* wb = s_kv[st_stage];
+    const int vo = sv_stage * kKBytes;   // V^T stage read
+    const int wo = st_stage * kKBytes;   // stage written
     uint4 va[2][4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) va[0][db] = lds_read16(vb + vr_off[db][0]);
+    for (int db = 0; db < 4; ++db) va[0][db] = lds_read16(vr_a[db][0], vo);
     uint32_t vw[2][4];
     // slot s: k-step k2 = s / 4. A bf16 cache: (s % 4) = high part of dims
     // blocks 0,1 / 2,3, then the residual of 0,1 / 2,3. 8-bit caches: one
@@ -560,7 +587,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       const int k2 = sl >> 2, q = sl & 3;
       if (sl == 0) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) va[1][db] = lds_read16(vb + vr_off[db][1]);
+        for (int db = 0; db < 4; ++db) va[1][db] = lds_read16(vr_a[db][1], vo);
       }
       if constexpr (kScaled) {
         o[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, va[k2][q]),
@@ -575,14 +602,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       }
       // staging of tile j + 2 (st -> LDS stage st_stage), then tile j + 3's loads
       if (sl < 2) {
-        *reinterpret_cast<uint4*>(wb + kw_off + 4096 * sl) = k_bf16(st, sl);
+        lds_write16(kw_a, wo + 4096 * sl, k_bf16(st, sl));
       } else if (sl == 2) {
         v_prep(st, vw);
       } else if (sl < 7) {
 #pragma unroll
         for (int e2 = 0; e2 < 2; ++e2) {
           const int e = 2 * (sl - 3) + e2;
-          *reinterpret_cast<uint32_t*>(wb + vw_off(e)) = v_word(st, vw, e);
+          lds_write4(vw_a[e], wo, v_word(st, vw, e));
         }
       } else {
         sc_store(st, st_stage);
@@ -636,24 +663,37 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   // MFMAs. The groups share no staged data; within a group the barriers
   // order the staging of a tile before its use and the reuse of a stage
   // after its last read. ----
-  int stj = 0;   // stage of this group's tile j
-  auto iter = [&](auto diag_tag, int j) {
-    const int st1 = stj == 2 ? 0 : stj + 1;
-    const int st2 = st1 == 2 ? 0 : st1 + 1;
+  // Tile j lives in stage j % 3. The loop over the tiles before the diagonal
+  // is unrolled by three so that its stages are compile-time constants: the
+  // stage offsets of its LDS accesses then sit in the instructions'
+  // immediate fields instead of being added per lane. The last (at most two)
+  // of those tiles and the (at most three) masked ones at the diagonal take
+  // their stage at run time.
+  auto iter = [&](auto diag_tag, auto stage, int j) {
+    const int S = stage;
+    const int S1 = (S + 1) % kStages, S2 = (S + 2) % kStages;
     TileSrc ns;
     tile_src(j + 3, ns);
     __builtin_amdgcn_sched_barrier(0);
-    phase1(diag_tag, j, st1, stj);
+    phase1(diag_tag, j, S1, S);
     __syncthreads();
-    phase2(j, stj, st2, sa, ns);
-    stj = st1;
+    phase2(j, S, S2, sa, ns);
     __syncthreads();
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   if (th == 1) __syncthreads();
   const int fdc = min(first_diag, ntiles);
   int j = 0;
-  for (; j < fdc; ++j) iter(std::false_type{}, j);
-  for (; j < ntiles; ++j) iter(std::true_type{}, j);
+  // tiles before the diagonal: stages 0, 1, 2 in turn from tile 0
+  for (; j + 3 <= fdc; j += 3) {
+    iter(std::false_type{}, I0{}, j);
+    iter(std::false_type{}, I1{}, j + 1);
+    iter(std::false_type{}, I2{}, j + 2);
+  }
+  for (; j < fdc; ++j) iter(std::false_type{}, j % kStages, j);
+  for (; j < ntiles; ++j) iter(std::true_type{}, j % kStages, j);
   if (th == 0) __syncthreads();
 
   // ---- merge the two token halves: wavefront w + 4 hands (o, m, l) to w ----
