@@ -148,6 +148,19 @@ __device__ __forceinline__ uint32_t lane_address(uint32_t a) {
   asm volatile("" : "+v"(a));
   return a;
 }
+// max / sum of x over lanes l and l ^ 32, in every lane: gfx950's
+// v_permlane32_swap exchanges the upper half of one register with the lower
+// half of another, so with x in both each lane sees {x[l], x[l ^ 32]} (a VALU
+// exchange, not an LDS round trip)
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ uint4 lds_read16(uint32_t a, int off) {
   const u32x4v_t x = *reinterpret_cast<const __attribute__((address_space(3))) u32x4v_t*>((const lds_char*)(uintptr_t)a + off);
   return make_uint4(x.x, x.y, x.z, x.w);
@@ -514,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     for (int c = 0; c < 4; ++c) {
       mfma1(4 + c);
       if (c == 0) {
-        float tmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+        float tmax = xor32_max(cmax);
         if constexpr (!kScaled) tmax *= p.scale_log2;   // the max commutes with a positive scale
         // move the reference max only when the tile exceeds it by more than
         // the slack: weights stay below 2^kSlack and O is rarely rescaled
@@ -552,7 +565,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    rsum += __shfl_xor(rsum, 32);
+    rsum = xor32_sum(rsum);
     l += rsum;
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
