@@ -61,6 +61,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+# The mixed step leaves the decode rows' split to the caller. Measured on
+# MI355X (int8, decode launch alone): 110.5 us with 512-token splits, 104.1 with
+# 1024, 103.9 with 1536, 108.1 with 2048 and 123.5 with one split per sequence:
+# longer splits spread each workgroup's start-up over more blocks until too few
+# workgroups are left to fill the GPU.
+MIXED_SPLIT = 1024
+
 # name -> (builder(seed, max_tokens_per_split), default replicas, default split size, config text)
 WORKLOADS = {
     "qwen3_decode": (lambda W, seed, mts, batch, r: W.qwen3_decode(batch=batch, seed=seed, values_seed=seed + 1000 * r,
@@ -74,18 +81,19 @@ WORKLOADS = {
                                                                   num_splits=(32768 // mts) if mts else 64),
                     1, 512, {"workload": "long_decode_b8_32k", "context_lens": "32768"}),
     "mixed_int8_decode": (lambda W, seed, mts, batch, r: W.mixed_int8(seed=seed + 1000 * r,
-                                                                       max_tokens_per_split=mts or 512),
-                          1, 512, {"workload": "mixed_int8_step_decode_rows", "context_lens": "uniform[256,4096]"}),
+                                                                       max_tokens_per_split=mts or MIXED_SPLIT),
+                          1, MIXED_SPLIT, {"workload": "mixed_int8_step_decode_rows", "context_lens": "uniform[256,4096]"}),
     "mixed_fp8_decode": (lambda W, seed, mts, batch, r: W.mixed_int8(seed=seed + 1000 * r, kv_dtype="fp8",
-                                                                      max_tokens_per_split=mts or 512),
-                         1, 512, {"workload": "mixed_fp8_step_decode_rows", "context_lens": "uniform[256,4096]"}),
+                                                                      max_tokens_per_split=mts or MIXED_SPLIT),
+                         1, MIXED_SPLIT, {"workload": "mixed_fp8_step_decode_rows", "context_lens": "uniform[256,4096]"}),
 }
 DEFAULT_SEEDS = {"qwen3_decode": 1902, "ragged_decode": 1903, "long_decode": 1904, "mixed_int8_decode": 1905,
                  "mixed_fp8_decode": 1905}
 # Decode mode measured fastest on MI355X per shape: one workgroup per
 # (split, kv head) for the Qwen3 step (one split per sequence), the uniform
-# long contexts and the int8 batch (512-token splits); the log-uniform ragged
-# batch gains from the balanced deal of tiles.
+# long contexts (64 splits of 512 tokens, as the workload states) and the
+# mixed step's decode rows (1024-token splits); the log-uniform ragged batch
+# gains from the balanced deal of tiles.
 DEFAULT_MODES = {"qwen3_decode": "splits", "ragged_decode": "balanced", "long_decode": "splits",
                  "mixed_int8_decode": "splits", "mixed_fp8_decode": "splits"}
 
@@ -100,7 +108,7 @@ def parse():
     ap.add_argument("--batch", type=int, default=32)
     ap.add_argument("--max-tokens-per-split", type=int, default=None,
                     help="num_splits[b] = ceil(n_b / this); 0 = one split per sequence "
-                         "(default: 0 for the Qwen3 step, 512 for the others)")
+                         "(default: 0 for the Qwen3 step, 1024 for the mixed step's decode rows, 512 for the others)")
     ap.add_argument("--steps-per-graph", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -298,7 +306,7 @@ def measure_chunked(dev, iters: int = 200, kv_dtype: str = "i8"):
 
     import paged_kv_attention_19_amd as pkv
     import workloads as W
-    step = W.mixed_int8(kv_dtype=kv_dtype)
+    step = W.mixed_int8(kv_dtype=kv_dtype, max_tokens_per_split=MIXED_SPLIT)
 
     def dt(a, kind):
         if kind == "bf16":
@@ -314,7 +322,7 @@ def measure_chunked(dev, iters: int = 200, kv_dtype: str = "i8"):
     qc, cu, tc, cc = dt(qc, "bf16"), dt(cu, "i32"), dt(tc, "i32"), dt(cc, "i32")
     max_q = int(np.diff(step.chunk_batch()[1]).max())
     qd, td, ctxd, nsd = step.decode_batch()
-    max_ns = int(nsd.max())   # the decode rows: ceil(n / 512) splits each
+    max_ns = int(nsd.max())   # the decode rows: ceil(n / MIXED_SPLIT) splits each
     qd, td, ctxd, nsd = dt(qd, "bf16"), dt(td, "i32"), dt(ctxd, "i32"), dt(nsd, "i32")
     out_c = torch.empty((qc.shape[0], 16, 128), dtype=torch.float32, device=dev)
     out_d = torch.empty((qd.shape[0], 16, 128), dtype=torch.float32, device=dev)
