@@ -57,6 +57,16 @@ def test_chunked_group_sizes(gpu, kv, Hq, Hkv):
     run_and_check(step, gpu)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
+def test_chunked_context_past_the_lds_block_ids(gpu, kv):
+    """A 70,000-token context (4,375 blocks): the kernel keeps the first 4,096
+    block ids in LDS and reads the rest from the table, in the tile loads and
+    (8-bit caches) in the scan of the V scales."""
+    step = W.make_step(f"longctx_{kv}", [70000, 300], [40, 20], num_q_heads=2, num_kv_heads=1, head_dim=128,
+                       kv_dtype=kv, src_dtype="bf16", seed=98)
+    run_and_check(step, gpu)
+
+
 def _scale_bf16(bits: np.ndarray, log2: int) -> np.ndarray:
     """bf16 values times 2^log2 (exact for these magnitudes)."""
     f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** log2)
