@@ -404,8 +404,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        log("bench.py measures one GPU: this build has no multi-GPU path (the decode shards by "
-            "sequence or KV head with no exchange; see the design notes). Run with --gpus 1.")
+        log("bench.py measures one GPU: the library has no multi-GPU path. Decode would shard by sequence or "
+            "by KV head with no exchange, and a long context by splits merged with pkv_lse_combine. "
+            "Run with --gpus 1.")
         sys.exit(2)
 
     if args.copy_calibration:
