@@ -39,10 +39,11 @@
 // and a share of the VALU / LDS work, fenced so the interleaving survives:
 //   1. the softmax of tile j's scores  ||  S^T of tile j + 1 (MFMA);
 //   2. O^T += V_j^T P_j^T (MFMA)       ||  tile j + 2: registers -> LDS.
-// Global loads run two iterations ahead, into two register sets, as buffer
-// loads whose range is the valid part of each block: rows past the context
-// and blocks outside the table come back as zeros with no branch, so every
-// tile issues the same loads and only the older set is waited for. An int8
+// A tile's global loads are issued at the end of phase 2, one iteration
+// before that tile is staged, into one register set (issuing them earlier in
+// the phase measured slower). They are buffer loads whose range is the valid
+// part of each block: rows past the context and blocks outside the table come
+// back as zeros with no branch, so every tile issues the same loads. An int8
 // or fp8 cache is dequantized on its way to LDS (int8 codes and E4M3 values
 // are exact in bf16 and in fp16; K goes to bf16 beside the bf16 q rows, V to
 // fp16): the K scale multiplies the score column, the V scale the weight.
