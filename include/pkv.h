@@ -214,6 +214,13 @@ pkv_status pkv_paged_attention_decode_append(const void* k_new, const void* v_ne
  *                  [total_q][num_q_heads] or NULL (natural log).
  *   Cache dtypes: BF16, I8 or FP8; head_dim 128; GQA group size in {1, 2, 4, 8}.
  *   A chunk longer than max_q_len or than its context yields NaN rows.
+ * Arithmetic: QK^T with bf16 MFMA (exact products, fp32 sums); softmax in
+ * fp32. The PV product's weights are bf16 pairs (a high part and its
+ * residual, ~2^-17) over a BF16 cache, and fp16 (rounded once, 2^-12, with
+ * the V scale folded in) over an I8 or FP8 cache, whose codes are exact in
+ * fp16. The output therefore agrees with exact attention over the cached
+ * values to about 2^-12 of |V| on rows that see few keys (less as more keys
+ * average), for V scales of any magnitude.
  */
 pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t num_seqs,
                                        int32_t num_q_heads, const int32_t* cu_q_lens,
