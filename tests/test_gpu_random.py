@@ -1,0 +1,96 @@
+"""GPU parity over seeded random configurations: every head_dim, GQA group
+size, cache and q dtype the library builds, random context lengths (block
+multiples and ragged tails), random split counts (past the block count too:
+empty splits), split and balanced decode modes, and random chunk / prefix
+lengths for chunked prefill. The cases are drawn once, from a fixed seed, so
+every run tests the same ones."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads as W
+from tests import gpu_side as G
+from tests import oracle_side as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_cases(n_cases: int = 24, seed: int = 20261202):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n_cases):
+        D = int(rng.choice([64, 128]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        hkv = int(rng.choice([1, 2, 4]))
+        kv = str(rng.choice(["f32", "bf16", "i8", "fp8"]))
+        qd = str(rng.choice(["f32", "bf16"]))
+        B = int(rng.integers(1, 13))
+        ctx = rng.integers(1, 701, size=B)
+        mult = rng.random(B) < 0.25                      # some contexts end on a block boundary
+        ctx[mult] = 16 * rng.integers(1, 44, size=int(mult.sum()))
+        blocks = -(-ctx // 16)
+        ns = np.minimum(rng.integers(1, 9, size=B), blocks + 1).astype(np.int32)
+        mode = str(rng.choice(["splits", "balanced"]))
+        cases.append(dict(id=f"d{i}_{mode}_D{D}_g{g}_h{hkv}_{kv}_q{qd}_B{B}", D=D, g=g, hkv=hkv, kv=kv, qd=qd,
+                          ctx=[int(c) for c in ctx], ns=[int(x) for x in ns], mode=mode, seed=3000 + i))
+    return cases
+
+
+def _chunked_cases(n_cases: int = 16, seed: int = 20261203):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n_cases):
+        g = int(rng.choice([1, 2, 4, 8]))
+        hkv = int(rng.choice([1, 2]))
+        kv = str(rng.choice(["bf16", "i8", "fp8"]))
+        S = int(rng.integers(1, 5))
+        L = rng.integers(2, 201, size=S)                 # (one-row sequences are decode rows)
+        prefix = rng.integers(0, 601, size=S)
+        cases.append(dict(id=f"c{i}_g{g}_h{hkv}_{kv}_S{S}", g=g, hkv=hkv, kv=kv,
+                          ctx=[int(a + b) for a, b in zip(prefix, L)], ql=[int(x) for x in L], seed=4000 + i))
+    return cases
+
+
+DECODE = _decode_cases()
+CHUNKED = _chunked_cases()
+
+
+def _check(out, ref, what, case):
+    st = O.compare(out, ref)
+    assert st["ok"], f"{case['id']} {what}: {st}"
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[c["id"] for c in DECODE])
+def test_random_decode(gpu, case):
+    import torch
+    scaled = case["kv"] in ("i8", "fp8")
+    step = W.make_step(case["id"], case["ctx"], [1] * len(case["ctx"]), num_q_heads=case["g"] * case["hkv"],
+                       num_kv_heads=case["hkv"], head_dim=case["D"], q_dtype=case["qd"], kv_dtype=case["kv"],
+                       src_dtype=(case["qd"] if scaled else case["kv"]), num_splits=case["ns"], seed=case["seed"])
+    cache = G.build_cache(step, gpu)
+    if case["mode"] == "splits":
+        out, lse = G.run_decode(step, cache, gpu)
+    else:
+        q, tables, ctx, _ = step.decode_batch()
+        G.announce(f"balanced decode {case['id']}")
+        out, lse = G.pkv.paged_attention_decode(G.tensor(q, step.q_dtype, gpu), cache, G.ints(tables, gpu),
+                                                G.ints(ctx, gpu), None, 0, float(step.scale), return_lse=True)
+        torch.cuda.synchronize()
+        out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    ro, rl = O.decode(step, O.pool(step))
+    _check(out, ro, "out", case)
+    _check(lse, rl, "lse", case)
+
+
+@pytest.mark.parametrize("case", CHUNKED, ids=[c["id"] for c in CHUNKED])
+def test_random_chunked(gpu, case):
+    step = W.make_step(case["id"], case["ctx"], case["ql"], num_q_heads=case["g"] * case["hkv"],
+                       num_kv_heads=case["hkv"], head_dim=128, kv_dtype=case["kv"], src_dtype="bf16",
+                       seed=case["seed"])
+    cache = G.build_cache(step, gpu)
+    out, lse = G.run_chunked(step, cache, gpu)
+    ro, rl = O.chunked(step, O.pool(step))
+    _check(out, ro, "out", case)
+    _check(lse, rl, "lse", case)
