@@ -318,6 +318,10 @@ def measure_chunked(dev, iters: int = 200, kv_dtype: str = "i8"):
                           dt(step.prefix_slots.astype(np.int64), "i64"), cache)
     new_k, new_v = dt(step.new_k, "bf16"), dt(step.new_v, "bf16")
     new_s = dt(step.new_slots.astype(np.int64), "i64")
+    # the step's new rows (the chunks' own K/V and the decode tokens) are in the
+    # cache before any pass reads it; the whole-step timing writes them again
+    # (the same bytes)
+    pkv.reshape_and_cache(new_k, new_v, new_s, cache)
     qc, cu, tc, cc = step.chunk_batch()
     qc, cu, tc, cc = dt(qc, "bf16"), dt(cu, "i32"), dt(tc, "i32"), dt(cc, "i32")
     max_q = int(np.diff(step.chunk_batch()[1]).max())
@@ -341,12 +345,17 @@ def measure_chunked(dev, iters: int = 200, kv_dtype: str = "i8"):
     for name, fn in (("chunked", chunked), ("step", whole)):
         fn()
         torch.cuda.synchronize()
+        eager = (out_c.clone(), out_d.clone())
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(20):
                 fn()
         g.replay()
         torch.cuda.synchronize()
+        # the replayed graph must reproduce the eager call bit for bit (and a
+        # NaN, from a pool row never written, fails the comparison)
+        if not torch.equal(out_c, eager[0]) or (name == "step" and not torch.equal(out_d, eager[1])):
+            raise RuntimeError(f"the {name} graph replay differs from the eager call")
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(max(1, iters // 20)):
