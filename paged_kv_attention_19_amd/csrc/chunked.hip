@@ -183,7 +183,12 @@ struct Staged {
   bool sc_ok;      // that token exists
 };
 
-template <int KV, int G>
+// kIdsInLds: every block id of the table fits the LDS copy (max_blocks <=
+// kIdsCached), so the tile loop reads ids from LDS only. A global load of an
+// id inside the loop would make the compiler wait for it with vmcnt(0), that
+// is, for every tile load in flight as well (vector memory counts retire in
+// order), and the loads issued for later tiles would lose their lead.
+template <int KV, int G, bool kIdsInLds>
 __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   constexpr int P = kRows / G;               // positions per query tile
   constexpr bool kScaled = is_scaled_kv(KV);   // int8 / fp8 codes + a scale per row
@@ -273,7 +278,21 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 
   // the block ids this tile range needs, read once into LDS (ids past what
   // LDS holds are read from the table when used)
-  for (int j = tid; j < min(nblk_need, kIdsCached); j += kThreads) s_ids[j] = trow[j];
+  {
+    // all of a thread's loads first, then the stores, so the loads overlap
+    const int nfill = min(nblk_need, kIdsCached);
+    int idv[kIdsCached / kThreads];
+#pragma unroll
+    for (int u = 0; u < kIdsCached / kThreads; ++u) {
+      const int j = tid + u * kThreads;
+      idv[u] = j < nfill ? trow[j] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kIdsCached / kThreads; ++u) {
+      const int j = tid + u * kThreads;
+      if (j < nfill) s_ids[j] = idv[u];
+    }
+  }
   __syncthreads();
 
   // Each group of 4 wavefronts (th = 0: wavefronts 0-3, th = 1: 4-7) loads
@@ -306,7 +325,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     int id = 0;
     rows = 0;
     if (blk < nblk_need) {
-      id = blk < kIdsCached ? s_ids[blk] : trow[blk];
+      id = (kIdsInLds || blk < kIdsCached) ? s_ids[blk] : trow[blk];
       id = __builtin_amdgcn_readfirstlane(id);
       if (static_cast<unsigned>(id) < static_cast<unsigned>(p.num_blocks)) {
         rows = min(kBlock, n - blk * kBlock);
@@ -643,12 +662,29 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     gload(0, sa);
     gload(1, sb);
     if constexpr (kScaled) {
-      for (int t = tid; t < kv_end; t += kThreads) {
-        const int blk = t / kBlock;
-        const int id = blk < kIdsCached ? s_ids[blk] : trow[blk];
-        if (static_cast<unsigned>(id) < static_cast<unsigned>(p.num_blocks)) {
-          vmax = fmaxf(vmax, p.v_scale[(static_cast<size_t>(id) * p.num_kv_heads + kh) * kBlock + t % kBlock]);
+      // in batches of 8 keys per thread whose loads are all issued before
+      // any is used
+      constexpr int kScan = 8;
+      for (int t0 = tid; t0 < kv_end; t0 += kScan * kThreads) {
+        int id[kScan];
+#pragma unroll
+        for (int u = 0; u < kScan; ++u) {
+          // ids straight from the (cache-hot) table, unconditionally: the
+          // block of min(t, kv_end - 1) is always one the range needs
+          const int t = t0 + u * kThreads;
+          const int raw = trow[min(t, kv_end - 1) / kBlock];
+          id[u] = t < kv_end ? raw : -1;
         }
+        float sv[kScan];
+#pragma unroll
+        for (int u = 0; u < kScan; ++u) {
+          const int t = t0 + u * kThreads;
+          sv[u] = static_cast<unsigned>(id[u]) < static_cast<unsigned>(p.num_blocks)
+                      ? p.v_scale[(static_cast<size_t>(id[u]) * p.num_kv_heads + kh) * kBlock + t % kBlock]
+                      : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kScan; ++u) vmax = fmaxf(vmax, sv[u]);
       }
     }
     lstore(sa, 0);
@@ -762,7 +798,11 @@ hipError_t launch_t(const ChunkedParams& p, hipStream_t st) {
   const int64_t items = static_cast<int64_t>(p.num_seqs) * p.num_kv_heads * QT;
   if (items > (int64_t(1) << 30)) return hipErrorInvalidValue;
   const int grid = static_cast<int>((items + kXcdsC - 1) / kXcdsC * kXcdsC);
-  hipLaunchKernelGGL((chunked_kernel<KV, G>), dim3(grid), dim3(kThreads), 0, st, p);
+  if (p.max_blocks <= kIdsCached) {
+    hipLaunchKernelGGL((chunked_kernel<KV, G, true>), dim3(grid), dim3(kThreads), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((chunked_kernel<KV, G, false>), dim3(grid), dim3(kThreads), 0, st, p);
+  }
   return hipGetLastError();
 }
 
