@@ -669,10 +669,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
         int id[kScan];
 #pragma unroll
         for (int u = 0; u < kScan; ++u) {
-          // ids straight from the (cache-hot) table, unconditionally: the
-          // block of min(t, kv_end - 1) is always one the range needs
+          // ids from LDS when they all fit there, else straight from the
+          // (cache-hot) table, unconditionally: the block of
+          // min(t, kv_end - 1) is always one the range needs
           const int t = t0 + u * kThreads;
-          const int raw = trow[min(t, kv_end - 1) / kBlock];
+          const int bi = min(t, kv_end - 1) / kBlock;
+          const int raw = kIdsInLds ? s_ids[bi] : trow[bi];
           id[u] = t < kv_end ? raw : -1;
         }
         float sv[kScan];
