@@ -1,5 +1,6 @@
 // Chunked prefill for gfx950: causal query chunks over a paged KV prefix,
-// with bf16 MFMA for both contractions.
+// with MFMA for both contractions (bf16; the PV product in fp16 over int8 and
+// fp8 caches).
 //
 // What is computed (course README "Build an LLM Inference Engine From
 // Scratch", curriculum S11 chunked prefill and S12 FlashAttention): the L new
@@ -34,8 +35,8 @@
 // k order the second product needs, so P never moves between lanes.
 //
 // Pipeline. K is staged row-major and V transposed (the token index must be
-// the MFMA k dimension) in a ring of three LDS stages, XOR-swizzled against
-// bank conflicts. Iteration j runs two phases, each written as slots of MFMAs
+// the MFMA k dimension), each in a ring of three LDS stages, XOR-swizzled
+// against bank conflicts. Iteration j runs two phases, each written as slots of MFMAs
 // and a share of the VALU / LDS work, fenced so the interleaving survives:
 //   1. the softmax of tile j's scores  ||  S^T of tile j + 1 (MFMA);
 //   2. O^T += V_j^T P_j^T (MFMA)       ||  tile j + 2: registers -> LDS.
