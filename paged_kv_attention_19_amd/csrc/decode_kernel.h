@@ -131,7 +131,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
     const int w_tail = has_tail ? ((n - 1) / kBlock - blk_lo) % NW : 0;
     if (s == s_tail && w == w_tail) {
       append_rows<KV, D>(p, b, kh, lane);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_s_waitcnt(0);   // the row stores have completed (a workgroup-scope fence does not wait for them)
     }
   }
 
@@ -427,7 +427,13 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the stores above have completed
+      // The arrival may be counted only once the partial's stores have
+      // completed: the last arrival, in any workgroup on any XCD, reads the
+      // partial as soon as it sees the count. The stores are agent-scope
+      // (written through to the coherent level), so waiting for them is the
+      // whole release; a workgroup-scope fence does not wait for them, and an
+      // agent-scope one would also write back the L2.
+      __builtin_amdgcn_s_waitcnt(0);
       int old = 0;
       int32_t* cnt = p.counters + static_cast<size_t>(sb) * Hkv + skh;
       if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -112,3 +112,21 @@ def test_balanced_repeats_and_graph_replays_bit_identically(gpu):
         assert torch.equal(out, ref)
     ctr = ws[: 32 * 16 * 4].view(torch.int32)
     assert int(ctr.abs().sum()) == 0
+
+
+def test_balanced_first_calls_on_fresh_workspaces_many_cuts(gpu):
+    """A batch wide enough for 512 workgroups cuts most sequences between
+    wavefronts. Each call runs on a freshly zeroed workspace, so a merge that
+    read a contributor's partial before its stores had landed would take
+    zeros and miss the oracle. Five first calls, each checked."""
+    import torch
+    step = W.make_step("cuts", np.full(128, 1100), np.ones(128, np.int64), num_q_heads=16, num_kv_heads=8,
+                       head_dim=128, kv_dtype="bf16", seed=150)
+    cache = G.build_cache(step, gpu)
+    ro, rl = O.decode(step, O.pool(step))
+    for i in range(5):
+        ws = torch.zeros(G.pkv.decode_workspace_bytes(128, 16, 128, 0), dtype=torch.uint8, device=gpu)
+        out, lse = run_balanced(step, cache, gpu, workspace=ws)
+        for got, ref in ((out, ro), (lse, rl)):
+            st = O.compare(got, ref)
+            assert st["ok"], (i, st)
