@@ -58,11 +58,13 @@ def test_chunked_group_sizes(gpu, kv, Hq, Hkv):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
-def test_chunked_context_past_the_lds_block_ids(gpu, kv):
-    """A 70,000-token context (4,375 blocks): the kernel keeps the first 4,096
-    block ids in LDS and reads the rest from the table, in the tile loads and
-    (8-bit caches) in the scan of the V scales."""
-    step = W.make_step(f"longctx_{kv}", [70000, 300], [40, 20], num_q_heads=2, num_kv_heads=1, head_dim=128,
+@pytest.mark.parametrize("n", [65536, 70000])
+def test_chunked_context_past_the_lds_block_ids(gpu, kv, n):
+    """A 65,536-token context fills the 4,096 block ids the kernel keeps in
+    LDS exactly (the variant that reads ids from LDS only); a 70,000-token one
+    (4,375 blocks) takes the variant that reads the ids past the first 4,096
+    from the table, in the tile loads and (8-bit caches) the V-scale scan."""
+    step = W.make_step(f"longctx_{kv}_{n}", [n, 300], [40, 20], num_q_heads=2, num_kv_heads=1, head_dim=128,
                        kv_dtype=kv, src_dtype="bf16", seed=98)
     run_and_check(step, gpu)
 
