@@ -232,9 +232,15 @@ struct WaveDecoder {
   // issued by the same instructions (past the end with a zero-size
   // descriptor), so the compiler's wait counts cover exactly the block being
   // reduced.
-  template <int PD>
+  // first_loads() runs once, right after the first tiles' loads are issued:
+  // loads that the reduction needs but the tile addresses do not (the q rows)
+  // go out there, so the tile loads do not queue behind them (vector memory
+  // counts retire in order, and the ids the tile addresses need are waited
+  // for with vmcnt(0) at the head of the stream).
+  template <int PD, typename FirstLoads>
   __device__ __forceinline__ void stream_blocks(const DecodeParams& p, int kh, const int32_t* trow, int stride,
-                                                int tok0, int count, int t1, bool use_early, int early, bool& bad) {
+                                                int tok0, int count, int t1, bool use_early, int early, bool& bad,
+                                                FirstLoads&& first_loads) {
     Tile ring[PD + 1];
     for (int c0 = 0; c0 < count; c0 += kWave) {
       const int cn = min(kWave, count - c0);
@@ -254,6 +260,7 @@ struct WaveDecoder {
       };
 #pragma unroll
       for (int k = 0; k < PD; ++k) issue(k, ring[k]);
+      if (c0 == 0) first_loads();
       for (int it = 0; it < cn; it += PD + 1) {
 #pragma unroll
         for (int k = 0; k <= PD; ++k) {

@@ -92,10 +92,9 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
   wd.init_lane();
   const int lane = wd.lane;
   const int h0 = kh * G;
-  wd.load_q(p.q, p.num_q_heads, b, h0);
 
   // Split 0 always starts at block 0, so its first table entries can be read
-  // in the same round trip as q and the context length (entries past the
+  // in the same round trip as the context length (entries past the
   // context are discarded once n is known; the row has max_blocks entries).
   int early_ids = 0;
   if (s == 0) {
@@ -139,8 +138,11 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
 
   // ---- stream this wave's blocks: blocks w, w + NW, ... of the split ----
   bool bad = bad_n;
+  // q is loaded after the first tiles' loads are issued (it is needed only
+  // once the first tile is reduced; a wavefront with no blocks never needs it)
   wd.template stream_blocks<PD>(p, kh, p.tables + static_cast<size_t>(b) * p.max_blocks + blk_lo + w, NW,
-                                t0 + w * kBlock, nb_w, t1, s == 0, early_ids, bad);
+                                t0 + w * kBlock, nb_w, t1, s == 0, early_ids, bad,
+                                [&] { wd.load_q(p.q, p.num_q_heads, b, h0); });
 
   // ---- merge: bring the wave's token slots to one reference max ----
   float M[G];
