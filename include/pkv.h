@@ -131,6 +131,22 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t he
                                   int32_t max_num_splits);
 
 /*
+ * The decode mode to use when the caller has no split plan of its own: the
+ * max_num_splits value to pass to pkv_paged_attention_decode with
+ * num_splits == NULL. Host-only; touches no device.
+ *   max_blocks_per_seq <= 64 : 1, one split per sequence. Each workgroup
+ *                              streams one (sequence, kv head), at most 16
+ *                              blocks per wavefront, with no merge.
+ *   otherwise                : 0, the balanced mode (its workspace from
+ *                              pkv_decode_workspace_bytes(..., 0)), which
+ *                              evens out long and short sequences.
+ * Every choice gives the same result up to rounding; this one only picks the
+ * faster launch on MI355X for the table width (block sizes of 16 tokens).
+ * Returns -1 (and sets pkv_last_error) for max_blocks_per_seq < 1.
+ */
+int32_t pkv_decode_default_max_num_splits(int32_t max_blocks_per_seq);
+
+/*
  * paged_attention_decode: one query row per sequence over its paged history,
  * split-K (flash-decoding) with a log-sum-exp merge.
  *   q            : [batch][num_q_heads][head_dim] of q_dtype (F32 or BF16), 16-byte aligned.

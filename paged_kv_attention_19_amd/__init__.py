@@ -69,6 +69,7 @@ _SIGS = {
     "pkv_version": ([], ctypes.c_char_p),
     "pkv_reshape_and_cache": ([_P, _P, _I32, _P, _I32, ctypes.POINTER(_Cache), _P], _I32),
     "pkv_decode_workspace_bytes": ([_I32, _I32, _I32, _I32], ctypes.c_size_t),
+    "pkv_decode_default_max_num_splits": ([_I32], _I32),
     "pkv_paged_attention_decode": ([_P, _I32, _I32, _I32, ctypes.POINTER(_Cache), _P, _I32, _P, _P, _I32,
                                     ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], _I32),
     "pkv_paged_attention_decode_append": ([_P, _P, _I32, _P, _P, _I32, _I32, _I32, ctypes.POINTER(_Cache), _P, _I32,
@@ -225,9 +226,18 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, head_dim: int, max_num_
     return int(lib().pkv_decode_workspace_bytes(batch, num_q_heads, head_dim, max_num_splits))
 
 
+def decode_default_max_num_splits(max_blocks_per_seq: int) -> int:
+    """The library's choice of decode mode for a table width, for calls
+    without a split plan: 1 (one split per sequence) or 0 (balanced)."""
+    r = int(lib().pkv_decode_default_max_num_splits(max_blocks_per_seq))
+    if r < 0:
+        raise PkvError(-1, lib().pkv_last_error().decode())
+    return r
+
+
 def paged_attention_decode(q: torch.Tensor, cache: KVCache, block_tables: torch.Tensor,
                            context_lens: torch.Tensor, num_splits: torch.Tensor | None,
-                           max_num_splits: int, scale: float, out: torch.Tensor | None = None,
+                           max_num_splits: int | str, scale: float, out: torch.Tensor | None = None,
                            out_lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                            return_lse: bool = False, partials_only: bool = False):
     """Decode attention: ``q [B][Hq][D]`` -> ``out [B][Hq][D]`` float32 (and lse).
@@ -235,6 +245,9 @@ def paged_attention_decode(q: torch.Tensor, cache: KVCache, block_tables: torch.
     ``max_num_splits=0`` with ``num_splits=None`` selects the balanced mode; a
     workspace passed for it must have been zero-filled once (every call
     leaves its counters at zero).
+
+    ``max_num_splits="auto"`` (with ``num_splits=None``) takes
+    :func:`decode_default_max_num_splits` of the table width.
 
     ``partials_only=True`` (needs ``max_num_splits > 1`` and a ``workspace``)
     runs only the split pass and returns ``(o_part [B][S][Hq][D],
@@ -262,6 +275,10 @@ def paged_attention_decode(q: torch.Tensor, cache: KVCache, block_tables: torch.
         raise ValueError("block_tables / context_lens batch mismatch")
     if D != cache.head_dim:
         raise ValueError(f"q head_dim {D} != cache head_dim {cache.head_dim}")
+    if max_num_splits == "auto":
+        if num_splits is not None:
+            raise ValueError('max_num_splits="auto" takes no num_splits')
+        max_num_splits = decode_default_max_num_splits(block_tables.shape[1])
     if num_splits is not None:
         _need(num_splits, "num_splits", (torch.int32,), 1)
         if num_splits.shape[0] != B:

@@ -286,6 +286,25 @@ static pkv_status run_split_decode(const char* fn, const void* q, int32_t q_dtyp
   return ok();
 }
 
+// One split per sequence while every table is at most 64 blocks (1024
+// tokens) wide: a workgroup then streams at most 16 blocks per wavefront and
+// the launch has no merge. Wider tables go to the balanced mode, which evens
+// out long and short sequences at the price of a cross-workgroup merge.
+// Measured on MI355X, decode launch alone (bf16, 16 q / 8 kv heads, D 128):
+// n in [128, 384] (24-block tables), B = 8 .. 128: 7.9 / 8.0 / 9.8 / 15.5 /
+// 26.6 us with one split against 22.1 / 20.8 / 22.6 / 28.2 / 41.9 us
+// balanced; 256 log-uniform n in [64, 8192] (512-block tables): 295 us
+// balanced against 333 us with one split.
+constexpr int kOneSplitMaxBlocks = 64;
+
+int32_t pkv_decode_default_max_num_splits(int32_t max_blocks_per_seq) {
+  if (max_blocks_per_seq < 1) {
+    fail(PKV_ERR_INVALID_ARG, "pkv_decode_default_max_num_splits: max_blocks_per_seq=%d", max_blocks_per_seq);
+    return -1;
+  }
+  return max_blocks_per_seq <= kOneSplitMaxBlocks ? 1 : 0;
+}
+
 pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
                                       const pkv_cache* cache, const int32_t* block_tables,
                                       int32_t max_blocks_per_seq, const int32_t* context_lens,

@@ -27,10 +27,18 @@ def test_library_exports_every_header_function():
     names = pkv.exported_symbols()
     assert {"pkv_reshape_and_cache", "pkv_paged_attention_decode", "pkv_paged_attention_decode_append",
             "pkv_paged_attention_chunked", "pkv_lse_combine", "pkv_decode_workspace_bytes", "pkv_last_error",
-            "pkv_version"} <= set(names)
+            "pkv_version", "pkv_decode_default_max_num_splits"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert "gfx950" in pkv.version()
+
+
+def test_default_decode_mode_by_table_width():
+    """One split per sequence up to 64-block (1024-token) tables, balanced
+    past that; a width below 1 is an error."""
+    assert [pkv.decode_default_max_num_splits(w) for w in (1, 24, 64, 65, 512, 2048)] == [1, 1, 1, 0, 0, 0]
+    with pytest.raises(pkv.PkvError, match="max_blocks_per_seq=0"):
+        pkv.decode_default_max_num_splits(0)
 
 
 def test_workspace_bytes():

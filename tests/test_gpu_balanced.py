@@ -130,3 +130,26 @@ def test_balanced_first_calls_on_fresh_workspaces_many_cuts(gpu):
         for got, ref in ((out, ro), (lse, rl)):
             st = O.compare(got, ref)
             assert st["ok"], (i, st)
+
+
+@pytest.mark.parametrize("make,mode", [
+    (lambda: W.qwen3_decode(), 1),                        # 24-block tables: one split per sequence
+    (lambda: W.ragged_decode(batch=24, seed=1913), 0),    # 512-block tables: balanced
+], ids=["qwen3_one_split", "ragged24_balanced"])
+def test_auto_mode_matches_oracle(gpu, make, mode):
+    """max_num_splits="auto" runs the mode the library picks for the table
+    width, and that mode matches the oracle."""
+    import torch
+    step = make()
+    cache = G.build_cache(step, gpu)
+    q, tables, ctx, _ = step.decode_batch()
+    assert G.pkv.decode_default_max_num_splits(tables.shape[1]) == mode
+    G.announce(f"auto-mode decode {step.name} B={len(ctx)} width={tables.shape[1]}")
+    out, lse = G.pkv.paged_attention_decode(G.tensor(q, step.q_dtype, gpu), cache, G.ints(tables, gpu),
+                                            G.ints(ctx, gpu), None, "auto", float(step.scale), return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = O.decode(step, O.pool(step))
+    st = O.compare(out.cpu().numpy(), ro)
+    assert st["ok"], st
+    st = O.compare(lse.cpu().numpy(), rl)
+    assert st["ok"], st
