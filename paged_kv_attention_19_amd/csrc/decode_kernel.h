@@ -27,37 +27,61 @@
 
 namespace pkv {
 
-// Append (split mode): the whole wavefront writes the new K and V rows of kv
-// head kh of sequence b to slot p.slots[b] (skipped when the slot is outside
-// the pool), with the same per-row arithmetic as reshape_and_cache.
+// Append (split mode): one wavefront writes the new K and V rows of kv head
+// kh of sequence b to slot p.slots[b] (skipped when the slot is outside the
+// pool), with the same per-row arithmetic as reshape_and_cache. The rows are
+// read as one 16-byte piece per lane (a row is at most 512 bytes, so K and V
+// take at most 64 pieces):
+//   scaled 8-bit caches: lanes [0, R) hold K's pieces, [R, 2R) V's, with
+//                        R = D / (source elements per 16 bytes);
+//   other caches       : the rows are copied as they are, K's pieces then V's.
+// Every lane loads: lanes past the row's pieces load one of them again (the
+// same lines, in bounds), so the load needs no branch and no merge of values
+// that would make the wavefront wait for it on the spot.
+template <int KV, int D>
+__device__ __forceinline__ uint4 load_new_piece(const DecodeParams& p, int b, int kh, int lane) {
+  const int64_t row = static_cast<int64_t>(b) * p.num_kv_heads + kh;
+  if constexpr (is_scaled_kv(KV)) {
+    const int esize = p.new_dtype == PKV_BF16 ? 2 : 4;
+    const int R = D * esize / 16;
+    const int i = lane % (2 * R);
+    const bool isv = i >= R;
+    return *reinterpret_cast<const uint4*>(static_cast<const char*>(isv ? p.v_new : p.k_new) + row * D * esize +
+                                           (i % R) * 16);
+  } else {
+    constexpr int kRowBytes = D * KvGeom<KV>::kEsize;
+    constexpr int kPieces = kRowBytes / 16;
+    static_assert(2 * kPieces <= kWave, "K and V pieces of a row fit one wavefront");
+    const int i = lane % (2 * kPieces);
+    const bool isv = i >= kPieces;
+    return *reinterpret_cast<const uint4*>(static_cast<const char*>(isv ? p.v_new : p.k_new) + row * kRowBytes +
+                                           (i % kPieces) * 16);
+  }
+}
+
 template <int SRC, int D, int KV>
-__device__ __forceinline__ void append_quant(const DecodeParams& p, int64_t row, int64_t dst_row, int lane) {
-  constexpr int R = D / KvGeom<SRC>::kEpl;   // lanes per row: K on lanes [0, R), V on [R, 2R)
+__device__ __forceinline__ void store_quant(const DecodeParams& p, uint4 piece, int64_t dst_row, int lane) {
+  constexpr int R = D / KvGeom<SRC>::kEpl;
   if (lane < 2 * R) {
     const bool isv = lane >= R;
-    quantize_row_piece<SRC, D, KV>(isv ? p.v_new : p.k_new, isv ? p.v_w : p.k_w, isv ? p.v_scale_w : p.k_scale_w,
-                                   row, dst_row, lane % R);
+    quantize_piece<SRC, D, KV>(piece, isv ? p.v_w : p.k_w, isv ? p.v_scale_w : p.k_scale_w, dst_row, lane % R);
   }
 }
 
 template <int KV, int D>
-__device__ __forceinline__ void append_rows(const DecodeParams& p, int b, int kh, int lane) {
-  const int64_t slot = p.slots[b];
+__device__ __forceinline__ void store_new_piece(const DecodeParams& p, uint4 piece, int64_t slot, int kh, int lane) {
   if (slot < 0 || slot >= p.num_slots) return;
-  const int64_t row = static_cast<int64_t>(b) * p.num_kv_heads + kh;
   const int64_t dst_row = ((slot / kBlock) * p.num_kv_heads + kh) * kBlock + slot % kBlock;
   if constexpr (is_scaled_kv(KV)) {
-    if (p.new_dtype == PKV_BF16) append_quant<PKV_BF16, D, KV>(p, row, dst_row, lane);
-    else append_quant<PKV_F32, D, KV>(p, row, dst_row, lane);
+    if (p.new_dtype == PKV_BF16) store_quant<PKV_BF16, D, KV>(p, piece, dst_row, lane);
+    else store_quant<PKV_F32, D, KV>(p, piece, dst_row, lane);
   } else {
     constexpr int kRowBytes = D * KvGeom<KV>::kEsize;
     constexpr int kPieces = kRowBytes / 16;
-    for (int i = lane; i < 2 * kPieces; i += kWave) {   // K pieces, then V pieces
-      const bool isv = i >= kPieces;
-      const int piece = isv ? i - kPieces : i;
-      const char* src = static_cast<const char*>(isv ? p.v_new : p.k_new) + row * kRowBytes + piece * 16;
-      char* dst = static_cast<char*>(isv ? p.v_w : p.k_w) + dst_row * kRowBytes + piece * 16;
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    if (lane < 2 * kPieces) {
+      const bool isv = lane >= kPieces;
+      *reinterpret_cast<uint4*>(static_cast<char*>(isv ? p.v_w : p.k_w) + dst_row * kRowBytes +
+                                (lane % kPieces) * 16) = piece;
     }
   }
 }
@@ -103,6 +127,18 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
   }
   const int n = p.ctx[b];
   const int ns = p.direct ? 1 : p.nsplits[b];
+  // The step's new rows and their slot go out in the same round trip: which
+  // wavefront writes them is known only once n is, and loading them then
+  // would cost that wavefront a round trip more than the others. The empty
+  // asm with a memory clobber keeps the compiler from sinking these loads
+  // into the branch that uses them.
+  uint4 new_piece{};
+  int64_t new_slot = -1;
+  if (p.k_new != nullptr) {
+    new_piece = load_new_piece<KV, D>(p, b, kh, lane);
+    new_slot = p.slots[b];
+  }
+  asm volatile("" ::: "memory");
   if (ns < 1 || s >= ns) return;  // not a split of this sequence (the merge checks ns)
 
   const bool bad_n = (n < 0) || (static_cast<int64_t>(n) > static_cast<int64_t>(p.max_blocks) * kBlock);
@@ -121,15 +157,15 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
   // Append: the wavefront that reads the block of token n - 1 (in split
   // (n - 1) / tps, where the block is dealt to wavefront (its index in the
   // split) % NW; trailing splits may be empty) writes the new rows first and
-  // waits for those stores to complete before it issues any load, so its read
-  // of the block sees them. No other wavefront reads that block. With no
+  // waits for those stores to complete before it issues any tile load, so its
+  // read of the block sees them. No other wavefront reads that block. With no
   // tokens to read, split 0's wavefront 0 writes them.
   if (p.k_new != nullptr) {
     const bool has_tail = !bad_n && n > 0;
     const int s_tail = has_tail ? (n - 1) / tps : 0;
     const int w_tail = has_tail ? ((n - 1) / kBlock - blk_lo) % NW : 0;
     if (s == s_tail && w == w_tail) {
-      append_rows<KV, D>(p, b, kh, lane);
+      store_new_piece<KV, D>(p, new_piece, new_slot, kh, lane);
       __builtin_amdgcn_s_waitcnt(0);   // the row stores have completed (a workgroup-scope fence does not wait for them)
     }
   }

@@ -19,17 +19,16 @@
 
 namespace pkv {
 
-// Lane r (0 .. R-1) of an aligned group of R lanes: row `row` of src_rows
-// ([rows][D] in SRC) -> codes_out[dst_row][D] and scales_out[dst_row].
+// Lane r (0 .. R-1) of an aligned group of R lanes, holding the 16 bytes
+// `raw` of elements [r EPL, (r + 1) EPL) of one row in SRC: the row's codes
+// -> codes_out[dst_row][D] and its scale -> scales_out[dst_row].
 template <int SRC, int D, int KV = PKV_I8>
-__device__ __forceinline__ void quantize_row_piece(const void* src_rows, void* codes_out, float* scales_out,
-                                                   int64_t row, int64_t dst_row, int r) {
+__device__ __forceinline__ void quantize_piece(uint4 raw, void* codes_out, float* scales_out, int64_t dst_row,
+                                               int r) {
   static_assert(is_scaled_kv(KV), "a scaled 8-bit cache");
   constexpr float kMaxCode = KV == PKV_I8 ? 127.0f : 448.0f;
   constexpr int EPL = KvGeom<SRC>::kEpl;  // source elements per lane (4 or 8)
   constexpr int R = D / EPL;              // lanes per row
-  const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const char*>(src_rows) +
-                                                    (row * D + r * EPL) * KvGeom<SRC>::kEsize);
   float x[EPL];
   unpack16<SRC>(raw, x);
   float amax = 0.f;
@@ -59,6 +58,16 @@ __device__ __forceinline__ void quantize_row_piece(const void* src_rows, void* c
     *reinterpret_cast<uint32_t*>(dst) = packed[0];
   }
   if (r == 0) scales_out[dst_row] = scale;
+}
+
+// The same, reading the piece from row `row` of src_rows ([rows][D] in SRC).
+template <int SRC, int D, int KV = PKV_I8>
+__device__ __forceinline__ void quantize_row_piece(const void* src_rows, void* codes_out, float* scales_out,
+                                                   int64_t row, int64_t dst_row, int r) {
+  constexpr int EPL = KvGeom<SRC>::kEpl;
+  const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const char*>(src_rows) +
+                                                    (row * D + r * EPL) * KvGeom<SRC>::kEsize);
+  quantize_piece<SRC, D, KV>(raw, codes_out, scales_out, dst_row, r);
 }
 
 }  // namespace pkv
