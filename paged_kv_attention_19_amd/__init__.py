@@ -252,6 +252,11 @@ def paged_attention_decode(q: torch.Tensor, cache: KVCache, block_tables: torch.
     ``partials_only=True`` (needs ``max_num_splits > 1`` and a ``workspace``)
     runs only the split pass and returns ``(o_part [B][S][Hq][D],
     lse_part [B][S][Hq])`` views of the workspace, for :func:`lse_combine`."""
+    if max_num_splits == "auto":
+        if num_splits is not None or partials_only:
+            raise ValueError('max_num_splits="auto" takes no num_splits and no partials_only')
+        _need(block_tables, "block_tables", (torch.int32,), 2)
+        max_num_splits = decode_default_max_num_splits(block_tables.shape[1])
     if partials_only:
         _need(q, "q", (torch.float32, torch.bfloat16), 3)
         B, Hq, D = q.shape
@@ -275,10 +280,6 @@ def paged_attention_decode(q: torch.Tensor, cache: KVCache, block_tables: torch.
         raise ValueError("block_tables / context_lens batch mismatch")
     if D != cache.head_dim:
         raise ValueError(f"q head_dim {D} != cache head_dim {cache.head_dim}")
-    if max_num_splits == "auto":
-        if num_splits is not None:
-            raise ValueError('max_num_splits="auto" takes no num_splits')
-        max_num_splits = decode_default_max_num_splits(block_tables.shape[1])
     if num_splits is not None:
         _need(num_splits, "num_splits", (torch.int32,), 1)
         if num_splits.shape[0] != B:

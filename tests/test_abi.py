@@ -140,6 +140,19 @@ def test_chunked_and_combine_reject_bad_arguments():
     assert L.pkv_lse_combine(FAKE, FAKE, 2, 4, 128, 0, FAKE, FAKE, None, None) == -1
 
 
+def test_auto_mode_argument_checks():
+    """"auto" resolves before anything else and refuses a split plan or the
+    partials-only mode (both need an explicit split count)."""
+    import torch
+    t = torch.zeros(2, 3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="auto"):
+        pkv.paged_attention_decode(None, None, t, t, t, "auto", 0.1)
+    with pytest.raises(ValueError, match="auto"):
+        pkv.paged_attention_decode(None, None, t, t, None, "auto", 0.1, partials_only=True)
+    with pytest.raises(ValueError, match="GPU"):   # then the tensors are checked as for any mode
+        pkv.paged_attention_decode(None, None, t, t, None, "auto", 0.1)
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(2, 4, 64)
