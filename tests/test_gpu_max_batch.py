@@ -1,4 +1,4 @@
-"""GPU parity at the largest batch the decode entry points accept (65535
+"""GPU parity at the largest batch and split count the decode entry points accept (65535
 sequences), in split mode (one and two splits) and in the balanced mode.
 The sequences hold 1 to 32 tokens whose blocks are drawn from a small pool
 written by reshape_and_cache, so the pool stays small while the batch,
@@ -54,4 +54,30 @@ def test_decode_at_max_batch(gpu, mode):
     st = O.compare(out_s, ro)
     assert st["ok"], st
     st = O.compare(lse_s, rl)
+    assert st["ok"], st
+
+
+def test_decode_at_max_split_count(gpu):
+    """max_num_splits = 65535, the largest accepted: nearly every split of
+    every sequence is empty and must carry no weight in the merge."""
+    import torch
+    base = W.make_step("maxs_pool", [512] * 4, [1] * 4, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                       kv_dtype="bf16", seed=63)
+    cache = G.build_cache(base, gpu)
+    _, base_tables, _, _ = base.decode_batch()
+    pool_ids = np.unique(base_tables[base_tables >= 0])
+    rng = np.random.default_rng(64)
+    ctx = np.array([1, 700, 1000], np.int32)
+    tables = pool_ids[rng.integers(0, len(pool_ids), size=(3, 63))].astype(np.int32)
+    ns = np.array([65535, 65535, 777], np.int32)
+    q_bits = W.f32_to_bf16_bits(rng.standard_normal((3, 4, 64)).astype(np.float32))
+    G.announce("decode with max_num_splits = 65535")
+    out, lse = G.pkv.paged_attention_decode(G.tensor(q_bits, "bf16", gpu), cache, G.ints(tables, gpu),
+                                            G.ints(ctx, gpu), G.ints(ns, gpu), 65535, float(base.scale),
+                                            return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_decode(oracle.decode_rows(q_bits, "bf16"), O.pool(base), tables, ctx, base.scale)
+    st = O.compare(out.cpu().numpy(), ro)
+    assert st["ok"], st
+    st = O.compare(lse.cpu().numpy(), rl)
     assert st["ok"], st
