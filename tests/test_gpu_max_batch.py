@@ -1,10 +1,12 @@
-"""GPU parity at the largest batch and split count the decode entry points accept (65535
-sequences), in split mode (one and two splits) and in the balanced mode.
-The sequences hold 1 to 32 tokens whose blocks are drawn from a small pool
-written by reshape_and_cache, so the pool stays small while the batch,
-the grid and the balanced mode's search over the batch are at full size.
-Sampled outputs (the first, the last and random ones) are checked against
-the oracle one by one."""
+"""GPU parity at the largest sizes the decode entry points accept.
+
+- Batch 65535, in split mode (one and two splits) and in the balanced mode.
+  The sequences hold 1 to 32 tokens whose blocks are drawn from a small pool
+  written by reshape_and_cache, so the pool stays small while the batch, the
+  grid and the balanced mode's search over the batch are at full size.
+  Sampled outputs (the first, the last and random ones) are checked against
+  the oracle one by one.
+- max_num_splits 65535, where nearly every split is empty."""
 
 from __future__ import annotations
 
