@@ -69,6 +69,18 @@ def test_chunked_context_past_the_lds_block_ids(gpu, kv, n):
     run_and_check(step, gpu)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (16, 2)])
+def test_chunked_full_prefill_one_long_chunk(gpu, kv, Hq, Hkv):
+    """A whole 4,096-token prompt as one chunk with no prefix: every query
+    tile's keys end on its own diagonal tile, and the causal mask covers the
+    whole range."""
+    L = 4096 if Hq == 2 else 1024
+    step = W.make_step(f"fullprefill_{kv}_{Hq}", [L], [L], num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,
+                       kv_dtype=kv, src_dtype="bf16", seed=77)
+    run_and_check(step, gpu)
+
+
 def _scale_bf16(bits: np.ndarray, log2: int) -> np.ndarray:
     """bf16 values times 2^log2 (exact for these magnitudes)."""
     f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** log2)
