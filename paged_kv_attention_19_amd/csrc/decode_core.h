@@ -27,6 +27,8 @@ namespace pkv {
 
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
 template <int KV, int QT, int D, int G>
 struct WaveDecoder {
   using Geo = KvGeom<KV>;
@@ -40,6 +42,10 @@ struct WaveDecoder {
   static constexpr int NE = CPL * EPL;                  // row elements per lane
   static constexpr int kTileBytes = kBlock * ROWB;
   static constexpr bool kDot2 = (KV == PKV_BF16 && QT == PKV_BF16);
+  // int8 K with bf16 q: q . k as two-wide fp16 dot products over the codes
+  // biased into fp16 (1152 + c, exact), q scaled by a power of two per lane
+  // into fp16 range (exact for bf16 values), the bias removed once per score
+  static constexpr bool kDot2I8 = (KV == PKV_I8 && QT == PKV_BF16);
   static constexpr bool kScaled = is_scaled_kv(KV);   // int8 / fp8 code + scale per row
   static constexpr float kRescaleSlack = 8.0f;
   static_assert(TPI * LPT == kWave && IPB * TPI == kBlock && IPB * CPL * 1024 == kTileBytes, "geometry");
@@ -55,6 +61,11 @@ struct WaveDecoder {
   int lane, tslot, lc, lane_off;
   float qf[G][NE];
   uint32_t q2[G][NE / 2];
+  // kDot2I8: q2 holds q's bf16 pairs until the first reduction after load_q
+  // turns them, in place, into fp16 pairs scaled by 2^sh (q_ready); qbias is
+  // 1152 times the sum of those values and qinv is 2^-sh
+  float qbias[G], qinv[G];
+  bool q_ready;
   float m[G], l[G], acc[G][NE];
 
   __device__ __forceinline__ void init_lane() {
@@ -66,17 +77,22 @@ struct WaveDecoder {
 
   // The G query rows of group kh of sequence b, on the lane's NE dims.
   __device__ __forceinline__ void load_q(const void* q, int num_q_heads, int b, int h0) {
+    q_ready = false;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         const size_t base = (static_cast<size_t>(b) * num_q_heads + h0 + g) * D + (j * LPT + lc) * EPL;
-        if constexpr (kDot2) {
-          const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + base);
-          q2[g][4 * j + 0] = x.x;
-          q2[g][4 * j + 1] = x.y;
-          q2[g][4 * j + 2] = x.z;
-          q2[g][4 * j + 3] = x.w;
+        if constexpr (kDot2 || kDot2I8) {
+          // the chunk's EPL bf16 values, 8 per 16-byte load
+#pragma unroll
+          for (int u = 0; u < EPL / 8; ++u) {
+            const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + base + 8 * u);
+            q2[g][j * (EPL / 2) + 4 * u + 0] = x.x;
+            q2[g][j * (EPL / 2) + 4 * u + 1] = x.y;
+            q2[g][j * (EPL / 2) + 4 * u + 2] = x.z;
+            q2[g][j * (EPL / 2) + 4 * u + 3] = x.w;
+          }
         } else if constexpr (QT == PKV_BF16) {
           const uint16_t* qp = static_cast<const uint16_t*>(q) + base;
 #pragma unroll
@@ -137,15 +153,58 @@ struct WaveDecoder {
     }
   }
 
+  // kDot2I8: q of each head in fp16 pairs. The lane's largest |q| is brought
+  // to [2^14, 2^15) by a power of two (exact for bf16 q; a value more than
+  // 2^28 below the largest may lose bits as an fp16 subnormal, far below the
+  // float32 rounding of the sum).
+  __device__ __forceinline__ void prepare_qh() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = 0.f;
+#pragma unroll
+      for (int e = 0; e < NE / 2; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(q2[g][e])), fabsf(bf16_hi(q2[g][e]))));
+      const int sh = mx > 0.f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < NE / 2; ++e) {
+        const _Float16 a = static_cast<_Float16>(__builtin_ldexpf(bf16_lo(q2[g][e]), sh));
+        const _Float16 c = static_cast<_Float16>(__builtin_ldexpf(bf16_hi(q2[g][e]), sh));
+        sum += static_cast<float>(a) + static_cast<float>(c);
+        const f16x2_t v = {a, c};
+        q2[g][e] = __builtin_bit_cast(uint32_t, v);
+      }
+      qbias[g] = 1152.0f * sum;
+      qinv[g] = __builtin_ldexpf(1.0f, -sh);
+    }
+    q_ready = true;
+  }
+
   // One block of t.rows tokens (the rest of the tile is masked). The masked
   // rows were read as 0 (K, V and the 8-bit caches' scales), so they add exact zeros:
   // their weights are exp2(-inf) = 0 and their values are finite.
   __device__ __forceinline__ void process(const Tile& t, float scale_log2) {
+    if constexpr (kDot2I8) {
+      if (!q_ready) prepare_qh();
+    }
     float sc[IPB][G];
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
       float kf[NE];
-      if constexpr (!kDot2) {
+      uint32_t kh16[NE / 2];
+      if constexpr (kDot2I8) {
+        // codes with the sign bit flipped (c + 128) under the fp16 exponent
+        // byte 0x64: the fp16 numbers 1024 + c + 128, two per word
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const uint32_t w[4] = {t.k[i][j].x ^ 0x80808080u, t.k[i][j].y ^ 0x80808080u, t.k[i][j].z ^ 0x80808080u,
+                                 t.k[i][j].w ^ 0x80808080u};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kh16[j * 8 + 2 * e] = __builtin_amdgcn_perm(0x64646464u, w[e], 0x04010400u);
+            kh16[j * 8 + 2 * e + 1] = __builtin_amdgcn_perm(0x64646464u, w[e], 0x04030402u);
+          }
+        }
+      } else if constexpr (!kDot2) {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) unpack16<KV>(t.k[i][j], kf + j * EPL);
       }
@@ -153,7 +212,13 @@ struct WaveDecoder {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float d = 0.f;
-        if constexpr (kDot2) {
+        if constexpr (kDot2I8) {
+#pragma unroll
+          for (int e = 0; e < NE / 2; ++e)
+            d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q2[g][e]), __builtin_bit_cast(f16x2_t, kh16[e]), d,
+                                       false);
+          d = (d - qbias[g]) * qinv[g];
+        } else if constexpr (kDot2) {
 #pragma unroll
           for (int j = 0; j < CPL; ++j) {
             const uint32_t kw[4] = {t.k[i][j].x, t.k[i][j].y, t.k[i][j].z, t.k[i][j].w};
