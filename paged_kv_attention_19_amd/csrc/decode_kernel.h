@@ -305,11 +305,19 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
   const int Hq = p.num_q_heads;
 
   // ---- total tiles of the batch ----
+  // the context lengths are read kRound * 64 at a time, every load of a
+  // round issued before any is used (one round trip per 256 sequences)
+  constexpr int kRound = 4;
   int64_t T = 0;
-  for (int c0 = 0; c0 < p.batch; c0 += kWave) {
-    const int bb = c0 + lane;
-    const int nb = bb < p.batch ? blocks_of(p.ctx[bb], p.max_blocks) : 0;
-    T += wave_sum_i32(nb);
+  for (int c0 = 0; c0 < p.batch; c0 += kRound * kWave) {
+    int len[kRound];
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) {
+      const int bb = c0 + u * kWave + lane;
+      len[u] = bb < p.batch ? p.ctx[bb] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) T += wave_sum_i32(blocks_of(len[u], p.max_blocks));
   }
   T = uniform64(T) * Hkv;   // the same on every lane: scalar registers
 
@@ -337,19 +345,31 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
   // ---- locate tile r0: sequence b, kv head kh, block blk ----
   int b = 0;
   int64_t base = 0;   // flat index of tile (b, kh = 0, blk = 0)
-  for (int c0 = 0; c0 < p.batch; c0 += kWave) {
-    const int bb = c0 + lane;
-    const int tiles = bb < p.batch ? Hkv * blocks_of(p.ctx[bb], p.max_blocks) : 0;
-    const int incl = wave_incl_scan_i32(tiles, lane);
-    const int total = __shfl(incl, kWave - 1);
-    if (base + total > r0) {
-      const uint64_t hit = __ballot(base + incl > r0);
-      const int first = __builtin_ctzll(hit);
-      b = c0 + first;
-      base += __shfl(incl, first) - __shfl(tiles, first);
-      break;
+  bool found = false;
+  for (int c0 = 0; c0 < p.batch && !found; c0 += kRound * kWave) {
+    int len[kRound];
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) {
+      const int bb = c0 + u * kWave + lane;
+      len[u] = bb < p.batch ? p.ctx[bb] : 0;
     }
-    base += total;
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) {
+      if (!found) {
+        const int tiles = Hkv * blocks_of(len[u], p.max_blocks);   // 0 past the batch
+        const int incl = wave_incl_scan_i32(tiles, lane);
+        const int total = __shfl(incl, kWave - 1);
+        if (base + total > r0) {
+          const uint64_t hit = __ballot(base + incl > r0);
+          const int first = __builtin_ctzll(hit);
+          b = c0 + u * kWave + first;
+          base += __shfl(incl, first) - __shfl(tiles, first);
+          found = true;
+        } else {
+          base += total;
+        }
+      }
+    }
   }
   // the cursors are the same on every lane: keep them in scalar registers,
   // so the tile addresses built from them (buffer descriptors) are uniform
