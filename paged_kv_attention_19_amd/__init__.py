@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "F32", "BF16", "I8", "FP8", "PkvError", "KVCache", "lib", "library_path", "exported_symbols",
-    "reshape_and_cache", "decode_workspace_bytes", "paged_attention_decode",
+    "reshape_and_cache", "decode_workspace_bytes", "decode_default_max_num_splits", "paged_attention_decode",
     "paged_attention_decode_append", "paged_attention_chunked", "lse_combine", "version",
 ]
 
