@@ -25,7 +25,8 @@ import torch
 __all__ = [
     "F32", "BF16", "I8", "FP8", "PkvError", "KVCache", "lib", "library_path", "exported_symbols",
     "reshape_and_cache", "decode_workspace_bytes", "decode_default_max_num_splits", "paged_attention_decode",
-    "paged_attention_decode_append", "paged_attention_chunked", "lse_combine", "version",
+    "paged_attention_decode_append", "paged_attention_chunked", "lse_combine",
+    "version", "stream_read",
 ]
 
 F32, BF16, I8, FP8 = 0, 1, 2, 3
@@ -34,7 +35,7 @@ _CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.float8_
 _SCALED = (I8, FP8)   # 8-bit codes with a float32 scale per (token, kv head)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_HEADER = os.path.join(os.path.dirname(_HERE), "include", "pkv.h")
+_INCLUDE = os.path.join(os.path.dirname(_HERE), "include")
 
 
 def library_path() -> str:
@@ -77,6 +78,8 @@ _SIGS = {
     "pkv_paged_attention_chunked": ([_P, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Cache), _P, _I32, _P,
                                      ctypes.c_float, _P, _P, _P], _I32),
     "pkv_lse_combine": ([_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
+    "pkv_stream_read": ([_P, ctypes.c_size_t, _P, _P], _I32),
+    "pkv_stream_read_workgroups": ([ctypes.c_size_t], _I32),
 }
 
 
@@ -97,10 +100,13 @@ def lib():
 
 
 def exported_symbols() -> list[str]:
-    """Function names the public header declares."""
-    with open(_HEADER) as f:
-        text = f.read()
-    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+    """Function names the public headers (``include/*.h``) declare."""
+    names = set()
+    for h in sorted(os.listdir(_INCLUDE)):
+        if h.endswith(".h"):
+            with open(os.path.join(_INCLUDE, h)) as f:
+                names.update(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", f.read()))
+    return sorted(names)
 
 
 def version() -> str:
@@ -133,6 +139,51 @@ def _need(t: torch.Tensor, name: str, dtypes, ndim: int | None = None, device=No
         raise ValueError(f"{name} must be contiguous")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check_out(out, out_lse, rows: int, Hq: int, D: int, dev, return_lse: bool):
+    """Allocate or check ``out [rows][Hq][D]`` and ``out_lse [rows][Hq]`` (float32)."""
+    if out is None:
+        out = torch.empty((rows, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), 3)
+    if tuple(out.shape) != (rows, Hq, D):
+        raise ValueError(f"out shape {tuple(out.shape)}, expected {(rows, Hq, D)}")
+    if out_lse is None and return_lse:
+        out_lse = torch.empty((rows, Hq), dtype=torch.float32, device=dev)
+    if out_lse is not None:
+        _need(out_lse, "out_lse", (torch.float32,), 2)
+        if tuple(out_lse.shape) != (rows, Hq):
+            raise ValueError(f"out_lse shape {tuple(out_lse.shape)}, expected {(rows, Hq)}")
+    return out, out_lse
+
+
+def _check_decode_inputs(q, cache, block_tables, context_lens, num_splits):
+    """Host-side checks shared by every decode mode; returns ``(B, Hq, D)``."""
+    _need(q, "q", (torch.float32, torch.bfloat16), 3)
+    B, Hq, D = q.shape
+    _need(block_tables, "block_tables", (torch.int32,), 2)
+    _need(context_lens, "context_lens", (torch.int32,), 1)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens batch mismatch")
+    if D != cache.head_dim:
+        raise ValueError(f"q head_dim {D} != cache head_dim {cache.head_dim}")
+    if num_splits is not None:
+        _need(num_splits, "num_splits", (torch.int32,), 1)
+        if num_splits.shape[0] != B:
+            raise ValueError("num_splits batch mismatch")
+    return B, Hq, D
+
+
+def _check_workspace(workspace, need: int):
+    if workspace is None:
+        return 0
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    _need(workspace, "workspace", (workspace.dtype,))
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace of {nbytes} bytes, {need} needed")
+    return nbytes
 
 
 @dataclass
@@ -257,13 +308,14 @@ def paged_attention_decode(q: torch.Tensor, cache: KVCache, block_tables: torch.
             raise ValueError('max_num_splits="auto" takes no num_splits and no partials_only')
         _need(block_tables, "block_tables", (torch.int32,), 2)
         max_num_splits = decode_default_max_num_splits(block_tables.shape[1])
+    B, Hq, D = _check_decode_inputs(q, cache, block_tables, context_lens, num_splits)
     if partials_only:
-        _need(q, "q", (torch.float32, torch.bfloat16), 3)
-        B, Hq, D = q.shape
-        if max_num_splits < 2 or workspace is None:
+        if not isinstance(max_num_splits, int) or max_num_splits < 2 or workspace is None:
             raise ValueError("partials_only needs max_num_splits > 1 and a workspace")
+        if out is not None or out_lse is not None:
+            raise ValueError("partials_only writes the workspace only: pass no out / out_lse")
+        ws_bytes = _check_workspace(workspace, decode_workspace_bytes(B, Hq, D, max_num_splits))
         d = cache.descriptor()
-        ws_bytes = workspace.numel() * workspace.element_size()
         _check(lib().pkv_paged_attention_decode(
             q.data_ptr(), _CODE[q.dtype], B, Hq, ctypes.byref(d), block_tables.data_ptr(), block_tables.shape[1],
             context_lens.data_ptr(), _ptr(num_splits), max_num_splits, float(scale), None, None,
@@ -272,32 +324,12 @@ def paged_attention_decode(q: torch.Tensor, cache: KVCache, block_tables: torch.
         n_o = B * max_num_splits * Hq * D
         return (f[:n_o].view(B, max_num_splits, Hq, D),
                 f[n_o:n_o + B * max_num_splits * Hq].view(B, max_num_splits, Hq))
-    _need(q, "q", (torch.float32, torch.bfloat16), 3)
-    B, Hq, D = q.shape
-    _need(block_tables, "block_tables", (torch.int32,), 2)
-    _need(context_lens, "context_lens", (torch.int32,), 1)
-    if block_tables.shape[0] != B or context_lens.shape[0] != B:
-        raise ValueError("block_tables / context_lens batch mismatch")
-    if D != cache.head_dim:
-        raise ValueError(f"q head_dim {D} != cache head_dim {cache.head_dim}")
-    if num_splits is not None:
-        _need(num_splits, "num_splits", (torch.int32,), 1)
-        if num_splits.shape[0] != B:
-            raise ValueError("num_splits batch mismatch")
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    _need(out, "out", (torch.float32,), 3)
-    if tuple(out.shape) != (B, Hq, D):
-        raise ValueError("out shape")
-    if out_lse is None and return_lse:
-        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    if out_lse is not None:
-        _need(out_lse, "out_lse", (torch.float32,), 2)
+    out, out_lse = _check_out(out, out_lse, B, Hq, D, q.device, return_lse)
     need = decode_workspace_bytes(B, Hq, D, max_num_splits)
     if need and workspace is None:
         # zero-filled: the balanced mode's arrival counters must start at 0
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _check_workspace(workspace, need)
     d = cache.descriptor()
     _check(lib().pkv_paged_attention_decode(
         q.data_ptr(), _CODE[q.dtype], B, Hq, ctypes.byref(d), block_tables.data_ptr(), block_tables.shape[1],
@@ -316,8 +348,7 @@ def paged_attention_decode_append(k_new: torch.Tensor, v_new: torch.Tensor, slot
     sequence, at ``slot_mapping``) followed by :func:`paged_attention_decode`,
     in one pass. Split mode only (``max_num_splits >= 1``); ``partials_only``
     as for :func:`paged_attention_decode`."""
-    _need(q, "q", (torch.float32, torch.bfloat16), 3)
-    B, Hq, D = q.shape
+    B, Hq, D = _check_decode_inputs(q, cache, block_tables, context_lens, num_splits)
     _need(k_new, "k_new", (torch.float32, torch.bfloat16), 3)
     _need(v_new, "v_new", (k_new.dtype,), 3)
     _need(slot_mapping, "slot_mapping", (torch.int64,), 1)
@@ -325,34 +356,17 @@ def paged_attention_decode_append(k_new: torch.Tensor, v_new: torch.Tensor, slot
         raise ValueError(f"new rows are {tuple(k_new.shape)}, want ({B}, {cache.num_kv_heads}, {cache.head_dim})")
     if slot_mapping.shape[0] != B:
         raise ValueError("slot_mapping batch mismatch")
-    _need(block_tables, "block_tables", (torch.int32,), 2)
-    _need(context_lens, "context_lens", (torch.int32,), 1)
-    if block_tables.shape[0] != B or context_lens.shape[0] != B:
-        raise ValueError("block_tables / context_lens batch mismatch")
-    if D != cache.head_dim:
-        raise ValueError(f"q head_dim {D} != cache head_dim {cache.head_dim}")
-    if num_splits is not None:
-        _need(num_splits, "num_splits", (torch.int32,), 1)
-        if num_splits.shape[0] != B:
-            raise ValueError("num_splits batch mismatch")
     if partials_only:
         if max_num_splits < 2 or workspace is None:
             raise ValueError("partials_only needs max_num_splits > 1 and a workspace")
-        out = out_lse = None
+        if out is not None or out_lse is not None:
+            raise ValueError("partials_only writes the workspace only: pass no out / out_lse")
     else:
-        if out is None:
-            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-        _need(out, "out", (torch.float32,), 3)
-        if tuple(out.shape) != (B, Hq, D):
-            raise ValueError("out shape")
-        if out_lse is None and return_lse:
-            out_lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-        if out_lse is not None:
-            _need(out_lse, "out_lse", (torch.float32,), 2)
+        out, out_lse = _check_out(out, out_lse, B, Hq, D, q.device, return_lse)
     need = decode_workspace_bytes(B, Hq, D, max_num_splits) if max_num_splits > 0 else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _check_workspace(workspace, need)
     d = cache.descriptor()
     _check(lib().pkv_paged_attention_decode_append(
         k_new.data_ptr(), v_new.data_ptr(), _CODE[k_new.dtype], slot_mapping.data_ptr(),
@@ -374,19 +388,17 @@ def paged_attention_chunked(q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len:
     """Chunked prefill: ``q [sum L][Hq][D]`` bf16 -> ``out [sum L][Hq][D]`` float32 (and lse)."""
     _need(q, "q", (torch.bfloat16,), 3)
     T, Hq, D = q.shape
+    if D != cache.head_dim:
+        raise ValueError(f"q head_dim {D} != cache head_dim {cache.head_dim}")
     _need(cu_q_lens, "cu_q_lens", (torch.int32,), 1)
     S = cu_q_lens.shape[0] - 1
+    if S < 0:
+        raise ValueError("cu_q_lens needs num_seqs + 1 entries")
     _need(block_tables, "block_tables", (torch.int32,), 2)
     _need(context_lens, "context_lens", (torch.int32,), 1)
     if block_tables.shape[0] != S or context_lens.shape[0] != S:
         raise ValueError("block_tables / context_lens / cu_q_lens disagree on the sequence count")
-    if out is None:
-        out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
-    _need(out, "out", (torch.float32,), 3)
-    if out_lse is None and return_lse:
-        out_lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
-    if out_lse is not None:
-        _need(out_lse, "out_lse", (torch.float32,), 2)
+    out, out_lse = _check_out(out, out_lse, T, Hq, D, q.device, return_lse)
     d = cache.descriptor()
     _check(lib().pkv_paged_attention_chunked(
         q.data_ptr(), BF16, S, Hq, cu_q_lens.data_ptr(), int(max_q_len), ctypes.byref(d),
@@ -404,12 +416,26 @@ def lse_combine(o_part: torch.Tensor, lse_part: torch.Tensor, num_splits: torch.
     B, S, Hq, D = o_part.shape
     if tuple(lse_part.shape) != (B, S, Hq) or num_splits.shape[0] != B:
         raise ValueError("o_part / lse_part / num_splits shapes disagree")
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=o_part.device)
-    if out_lse is None:
-        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=o_part.device)
-    _need(out, "out", (torch.float32,), 3)
-    _need(out_lse, "out_lse", (torch.float32,), 2)
+    out, out_lse = _check_out(out, out_lse, B, Hq, D, o_part.device, True)
     _check(lib().pkv_lse_combine(o_part.data_ptr(), lse_part.data_ptr(), B, Hq, D, S, num_splits.data_ptr(),
                                  out.data_ptr(), out_lse.data_ptr(), _stream_handle()))
     return out, out_lse
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Measurement aid (``include/pkv_measure.h``): one launch that reads every
+    byte of ``src`` once and does nothing else. Returns the sink buffer (its
+    contents carry no meaning); pass one to allocate nothing."""
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    groups = int(lib().pkv_stream_read_workgroups(nbytes))
+    if sink is None:
+        sink = torch.empty(max(1, groups), dtype=torch.int32, device=src.device)
+    if sink.numel() * sink.element_size() < 4 * groups:
+        raise ValueError("sink too small")
+    st = int(lib().pkv_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), _stream_handle()))
+    if st != 0:
+        raise PkvError(st, "pkv_stream_read: bad arguments (16-byte aligned buffer of a multiple of 16 bytes) "
+                           "or launch failure")
+    return sink

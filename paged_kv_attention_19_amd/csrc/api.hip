@@ -99,9 +99,15 @@ int decode_waves(int /*max_blocks_per_seq*/, int /*max_num_splits*/) {
 // Balanced decode: 4 wavefronts per workgroup, 256 workgroups (one per CU)
 // or 512 for large batches; each wavefront owns two partial slots of
 // G (D + 1) floats (G <= Hq).
+// (pkv_decode_workspace_bytes knows only num_q_heads and sizes the slots for
+// a group of num_q_heads; the kernel uses group * (head_dim + 1) floats per
+// slot.)
 constexpr int kBalancedMaxWorkgroups = 512;
-size_t balanced_part_bytes(int num_q_heads, int head_dim) {
-  return static_cast<size_t>(kBalancedMaxWorkgroups) * 4 * 2 * num_q_heads * (head_dim + 1) * sizeof(float);
+size_t balanced_part_bytes(int heads_per_slot, int head_dim) {
+  return static_cast<size_t>(kBalancedMaxWorkgroups) * 4 * 2 * heads_per_slot * (head_dim + 1) * sizeof(float);
+}
+size_t balanced_counter_bytes(int batch, int num_q_heads) {
+  return (static_cast<size_t>(batch) * num_q_heads * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
 }
 int balanced_workgroups(int batch, int num_kv_heads, int max_blocks) {
   const int64_t tiles_bound = static_cast<int64_t>(batch) * num_kv_heads * max_blocks;
@@ -155,10 +161,7 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, int32_t s
 
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t max_num_splits) {
   if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_num_splits < 0) return 0;
-  if (max_num_splits == 0) {
-    const size_t counters = (static_cast<size_t>(batch) * num_q_heads * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
-    return counters + balanced_part_bytes(num_q_heads, head_dim);
-  }
+  if (max_num_splits == 0) return balanced_counter_bytes(batch, num_q_heads) + balanced_part_bytes(num_q_heads, head_dim);
   if (max_num_splits == 1) return 0;
   const size_t rows = static_cast<size_t>(batch) * max_num_splits * num_q_heads;
   const size_t bytes = rows * (static_cast<size_t>(head_dim) + 1) * sizeof(float);
@@ -286,6 +289,48 @@ static pkv_status run_split_decode(const char* fn, const void* q, int32_t q_dtyp
   return ok();
 }
 
+// Balanced mode (max_num_splits == 0): one launch; the workspace holds the
+// arrival counters (zero on entry), then the partial slots. The arguments have
+// been checked.
+static pkv_status run_balanced_decode(const char* fn, const void* q, int32_t q_dtype, int32_t batch,
+                                      int32_t num_q_heads, const pkv_cache* cache, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* context_lens, float scale,
+                                      float* out, float* out_lse, void* workspace, void* stream) {
+  const int D = cache->head_dim;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int group = num_q_heads / cache->num_kv_heads;
+  pkv::DecodeParams p{};
+  p.q = q;
+  p.k = cache->k;
+  p.v = cache->v;
+  p.k_scale = cache->k_scale;
+  p.v_scale = cache->v_scale;
+  p.tables = block_tables;
+  p.ctx = context_lens;
+  p.o = out;
+  p.lse = out_lse;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_blocks = cache->num_blocks;
+  p.max_ns = 0;
+  p.direct = 1;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.counters = static_cast<int32_t*>(workspace);
+  p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + balanced_counter_bytes(batch, num_q_heads));
+  const int wgs = balanced_workgroups(batch, cache->num_kv_heads, max_blocks_per_seq);
+  hipError_t e;
+  switch (cache->kv_dtype) {
+    case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, -wgs, st); break;
+    case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, -wgs, st); break;
+    case PKV_I8: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, -wgs, st); break;
+    default: e = pkv::launch_decode_partial_fp8(p, q_dtype, D, group, -wgs, st); break;
+  }
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
 // One split per sequence while every table is at most 64 blocks (1024
 // tokens) wide: a workgroup then streams at most 16 blocks per wavefront and
 // the launch has no merge. Wider tables go to the balanced mode, which evens
@@ -317,43 +362,9 @@ pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t ba
                                    &empty);
       st != PKV_OK || empty)
     return st;
-  const bool balanced = max_num_splits == 0;
-  const int D = cache->head_dim;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  const int group = num_q_heads / cache->num_kv_heads;
-  if (balanced) {
-    pkv::DecodeParams p{};
-    p.q = q;
-    p.k = cache->k;
-    p.v = cache->v;
-    p.k_scale = cache->k_scale;
-    p.v_scale = cache->v_scale;
-    p.tables = block_tables;
-    p.ctx = context_lens;
-    p.o = out;
-    p.lse = out_lse;
-    p.batch = batch;
-    p.num_q_heads = num_q_heads;
-    p.num_kv_heads = cache->num_kv_heads;
-    p.max_blocks = max_blocks_per_seq;
-    p.num_blocks = cache->num_blocks;
-    p.max_ns = 0;
-    p.direct = 1;
-    p.scale_log2 = scale * 1.4426950408889634f;
-    p.counters = static_cast<int32_t*>(workspace);
-    const size_t counters = (static_cast<size_t>(batch) * num_q_heads * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
-    p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + counters);
-    const int wgs = balanced_workgroups(batch, cache->num_kv_heads, max_blocks_per_seq);
-    hipError_t e;
-    switch (cache->kv_dtype) {
-      case PKV_F32: e = pkv::launch_decode_partial_f32(p, q_dtype, D, group, -wgs, st); break;
-      case PKV_BF16: e = pkv::launch_decode_partial_bf16(p, q_dtype, D, group, -wgs, st); break;
-      case PKV_I8: e = pkv::launch_decode_partial_i8(p, q_dtype, D, group, -wgs, st); break;
-      default: e = pkv::launch_decode_partial_fp8(p, q_dtype, D, group, -wgs, st); break;
-    }
-    if (e != hipSuccess) return hip_fail(e, fn);
-    return ok();
-  }
+  if (max_num_splits == 0)
+    return run_balanced_decode(fn, q, q_dtype, batch, num_q_heads, cache, block_tables, max_blocks_per_seq,
+                               context_lens, scale, out, out_lse, workspace, stream);
   return run_split_decode(fn, q, q_dtype, batch, num_q_heads, cache, block_tables, max_blocks_per_seq, context_lens,
                           num_splits, max_num_splits, scale, out, out_lse, workspace, nullptr, stream);
 }

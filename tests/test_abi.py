@@ -158,3 +158,16 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(2, 4, 64)
     with pytest.raises(ValueError, match="GPU"):
         pkv.paged_attention_decode(q, None, q, q, None, 1, 0.1)
+
+
+def test_stream_read_rejects_bad_arguments():
+    L = pkv.lib()
+    assert L.pkv_stream_read(None, 1024, FAKE, None) == -1
+    assert L.pkv_stream_read(FAKE, 1000, FAKE, None) == -1     # not a multiple of 16
+    assert L.pkv_stream_read(FAKE + 8, 1024, FAKE, None) == -1
+    assert L.pkv_stream_read(FAKE, 0, FAKE, None) == -1
+    assert L.pkv_stream_read(FAKE, 1024, None, None) == -1
+    assert L.pkv_stream_read_workgroups(0) == 0
+    assert L.pkv_stream_read_workgroups(16) == 1
+    assert L.pkv_stream_read_workgroups(34 << 20) == 2176      # 2,228,224 chunks / 1,024 per pass
+    assert L.pkv_stream_read_workgroups(1 << 30) == 4096
