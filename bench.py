@@ -8,7 +8,7 @@ sequences, 16 query / 8 KV heads, head_dim 128, bf16 q/K/V from N(0, 1),
 context lengths uniform in [128, 384], 16-token blocks drawn from a 4096-block
 pool. Inputs are resident in HBM before timing starts.
 
-One step's KV (33.6 MB) would sit in MI355X's 256 MB Infinity Cache if the
+One step's KV (34.4 MB) would sit in MI355X's 256 MB Infinity Cache if the
 same step were repeated, so the timed loop rotates through R replicas that
 stand for R layers of one model step: they share the batch's block tables,
 context lengths and slots (as an engine's layers do) and each owns its KV pool
@@ -16,6 +16,11 @@ and its q/K/V values. Between two uses of one replica the other R - 1 replicas
 stream well over 256 MB of KV, so every step reads its KV from HBM.
 Steps are launched from HIP graphs (each graph holds many steps) so that host
 launch cost does not pace the GPU.
+
+Timing: a window is exactly --steps steps, bracketed by HIP events on the
+stream the work runs on. Windows are replayed back to back until at least
+--min-seconds of GPU time and 5 windows have run (so a small --steps still
+gives a stable figure), and the median window gives the per-step time.
 
 Output: one JSON line on stdout (everything else goes to stderr).
 """
@@ -25,6 +30,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -35,11 +41,15 @@ if ROOT not in sys.path:
 
 METRIC = "paged-attn decode KV GB/s (% HBM peak) + seq-steps/s; chunked-prefill MFMA util"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
-KERNEL_FILES = ("paged_kv_attention_19_amd/csrc/decode_kernel.h", "paged_kv_attention_19_amd/csrc/decode_core.h",
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16, published
+DECODE_FILES = ("paged_kv_attention_19_amd/csrc/decode_kernel.h", "paged_kv_attention_19_amd/csrc/decode_core.h",
                 "paged_kv_attention_19_amd/csrc/decode_bf16.hip", "paged_kv_attention_19_amd/csrc/pkv_device.h",
                 "paged_kv_attention_19_amd/csrc/quant_row.h", "paged_kv_attention_19_amd/csrc/api.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_qwen3_traffic.json")
+CHUNKED_FILES = ("paged_kv_attention_19_amd/csrc/chunked.hip", "paged_kv_attention_19_amd/csrc/pkv_device.h",
+                 "paged_kv_attention_19_amd/csrc/api.hip")
+DECODE_PROFILE = os.path.join(ROOT, "profiles", "decode_partial_qwen3_traffic.json")
+CHUNKED_PROFILE = os.path.join(ROOT, "profiles", "chunked_kernel_mixed_int8_traffic.json")
+WINDOWS_MIN = 5
 
 
 def log(*a):
@@ -53,12 +63,33 @@ def kv_bytes_per_token(num_kv_heads: int, head_dim: int, elem_bytes: int, scale_
     return layers * 2 * num_kv_heads * (head_dim * elem_bytes + scale_bytes)
 
 
-def kernel_source_hash() -> str:
+def source_hash(files) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_FILES:
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def kernel_source_hash() -> str:
+    return source_hash(DECODE_FILES)
+
+
+def profile_figures(path: str, files, **match):
+    """Counter / trace figures recorded in profiles/ for the current sources
+    of a kernel (None if the kernel changed since they were taken, or if the
+    profile was taken on another configuration)."""
+    try:
+        with open(path) as f:
+            tr = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if tr.get("kernel_source_hash") != source_hash(files):
+        return None
+    for k, v in match.items():
+        if tr.get(k) != v:
+            return None
+    return tr
 
 
 # The mixed step leaves the decode rows' split to the caller. Measured on
@@ -68,7 +99,7 @@ def kernel_source_hash() -> str:
 # workgroups are left to fill the GPU.
 MIXED_SPLIT = 1024
 
-# name -> (builder(seed, max_tokens_per_split), default replicas, default split size, config text)
+# name -> (builder(W, seed, max_tokens_per_split, batch, replica), default replicas, default split size, config)
 WORKLOADS = {
     "qwen3_decode": (lambda W, seed, mts, batch, r: W.qwen3_decode(batch=batch, seed=seed, values_seed=seed + 1000 * r,
                                                                     max_tokens_per_split=mts or None),
@@ -96,13 +127,18 @@ DEFAULT_SEEDS = {"qwen3_decode": 1902, "ragged_decode": 1903, "long_decode": 190
 # gains from the balanced deal of tiles.
 DEFAULT_MODES = {"qwen3_decode": "splits", "ragged_decode": "balanced", "long_decode": "splits",
                  "mixed_int8_decode": "splits", "mixed_fp8_decode": "splits"}
+# the other decode configurations reported beside the headline one (each in
+# its default mode and split plan)
+OTHER_CONFIGS = ("ragged_decode", "long_decode", "mixed_int8_decode")
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=8192)
+    ap.add_argument("--steps", type=int, default=8192, help="steps per timed window")
     ap.add_argument("--warmup", type=int, default=512)
+    ap.add_argument("--min-seconds", type=float, default=0.25,
+                    help="windows of --steps steps are timed until at least this much GPU time (and 5 windows)")
     ap.add_argument("--replicas", type=int, default=None,
                     help="independent copies rotated through (default: 16 for the Qwen3 step, else 1)")
     ap.add_argument("--batch", type=int, default=32)
@@ -110,9 +146,11 @@ def parse():
                     help="num_splits[b] = ceil(n_b / this); 0 = one split per sequence "
                          "(default: 0 for the Qwen3 step, 1024 for the mixed step's decode rows, 512 for the others)")
     ap.add_argument("--steps-per-graph", type=int, default=256)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunked", action="store_true", help="skip the chunked-prefill MFMA measurement")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other decode configurations and the speculative-verify shape")
     ap.add_argument("--chunked-kv", choices=("i8", "fp8"), default="i8",
                     help="KV cache dtype of the mixed step in the chunked-prefill measurement")
     ap.add_argument("--no-fuse", action="store_true",
@@ -142,25 +180,63 @@ def copy_calibration(nbytes: int) -> None:
     print(json.dumps({"copy_bytes": nbytes, "copies": 8}), flush=True)
 
 
-def copy_reference(nbytes: int):
-    """A plain device-to-device copy that moves the same number of HBM bytes as
-    one decode launch (nbytes / 2 read, nbytes / 2 written), rotated over
-    enough buffers that every copy comes from HBM: the rate a memory-bound
-    kernel of this size can reach on this machine with no attention work."""
+def time_windows(fn_per_step, reps, steps, steps_per_graph, warmup, min_seconds):
+    """Time windows of exactly ``steps`` consecutive steps (rotating over the
+    replicas), captured in HIP graphs of at most ``steps_per_graph`` steps, and
+    replayed back to back until at least ``min_seconds`` of GPU time and
+    WINDOWS_MIN windows have run. Returns (median seconds per window, windows,
+    total timed seconds)."""
     import torch
-    copies, steps = (16, 2048) if nbytes < (64 << 20) else (2, 64)
-    half = max(16, (nbytes // 2) // 16 * 16)
-    pairs = [(torch.randint(0, 255, (half,), dtype=torch.uint8, device="cuda:0"),
-              torch.empty(half, dtype=torch.uint8, device="cuda:0")) for _ in range(copies)]
-    sec = time_graphs(lambda pr: pr[1].copy_(pr[0]), pairs, steps, 256, 64)
-    us = sec / steps * 1e6
-    return {"bytes_moved": 2 * half, "us": round(us, 3), "GB/s": round(2 * half / (sec / steps) / 1e9, 1)}
+    R = len(reps)
+
+    def capture(n, start):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn_per_step(reps[(start + i) % R])
+        return g
+
+    per = max(1, min(steps_per_graph, steps))
+    per = max(R, (per // R) * R)          # whole rotations inside a graph
+    n_full = steps // per
+    rem = steps % per
+    g_full = capture(per, 0) if n_full else None
+    g_rem = capture(rem, 0) if rem else None
+
+    def window():
+        for _ in range(n_full):
+            g_full.replay()
+        if g_rem is not None:
+            g_rem.replay()
+
+    torch.cuda.synchronize()
+    for _ in range(max(1, -(-warmup // max(1, steps)))):
+        window()
+    torch.cuda.synchronize()
+    # one window to size the run
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    window()
+    b.record()
+    torch.cuda.synchronize()
+    one = max(a.elapsed_time(b) / 1e3, 1e-7)
+    nwin = max(WINDOWS_MIN, math.ceil(min_seconds / one))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nwin + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(nwin):
+        window()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    secs = sorted(ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(nwin))
+    total = ev[0].elapsed_time(ev[-1]) / 1e3
+    return secs[nwin // 2], nwin, total
 
 
 class Replica:
     """One independent copy of the workload, resident on the GPU."""
 
-    def __init__(self, step, dev, max_tokens_per_split, balanced=False, fuse=True):
+    def __init__(self, step, dev, balanced=False, fuse=True):
         import numpy as np
         import torch
 
@@ -251,38 +327,99 @@ class Replica:
             self.decode()
 
 
-def time_graphs(fn_per_step, reps, steps, steps_per_graph, warmup):
-    """Capture graphs of ``steps_per_graph`` consecutive steps (rotating over the
-    replicas) and replay them until exactly ``steps`` steps ran; returns seconds."""
+def build_replicas(W, dev, workload, replicas, mts, batch, mode, fuse, seed=None):
+    build, _, _, _ = WORKLOADS[workload]
+    seed0 = DEFAULT_SEEDS[workload] if seed is None else seed
+    return [Replica(build(W, seed0, mts, batch, r), dev, balanced=mode == "balanced", fuse=fuse)
+            for r in range(replicas)]
+
+
+def check_replays_against_eager(reps, per_step, steps, steps_per_graph):
+    """An eager step per replica, then graph replays of the same steps: the
+    outputs must agree bit for bit (a NaN from an unwritten pool row fails
+    the comparison too)."""
     import torch
+    for r in reps:
+        per_step(r)
+    torch.cuda.synchronize()
+    eager = [(r.out.clone(), r.lse.clone()) for r in reps]
+    for r in reps:
+        r.out.fill_(float("nan"))
+        r.lse.fill_(float("nan"))
+    time_windows(per_step, reps, max(len(reps), min(steps, steps_per_graph)), steps_per_graph, 0, 0.0)
+    for r, (eo, el) in zip(reps, eager):
+        if not (torch.equal(r.out, eo) and torch.equal(r.lse, el)):
+            raise RuntimeError("graph replay output differs from the eager step")
+
+
+def stream_reference(nbytes: int, min_seconds: float):
+    """A read-only stream over the same number of bytes as one decode launch
+    reads (pkv_stream_read: 16-byte non-temporal loads and nothing else),
+    rotated over enough buffers (>= 1 GiB in all) that every launch reads
+    from HBM, graph-replayed like the decode: what a kernel that only reads
+    these bytes reaches on this machine, launch and drain included."""
+    import torch
+
+    import paged_kv_attention_19_amd as pkv
+    nb = max(16, (int(nbytes) // 16) * 16)
+    copies = max(1, min(16, math.ceil((1 << 30) / nb)))
+    bufs = []
+    for _ in range(copies):
+        src = torch.randint(-128, 127, (nb,), dtype=torch.int8, device="cuda:0")
+        sink = torch.zeros(max(1, int(pkv.lib().pkv_stream_read_workgroups(nb))), dtype=torch.int32, device="cuda:0")
+        bufs.append((src, sink))
+    steps = max(copies, 64 * copies if nb < (64 << 20) else 4 * copies)
+    sec, nwin, _ = time_windows(lambda b: pkv.stream_read(b[0], b[1]), bufs, steps, 256, steps, min_seconds)
+    per = sec / steps
+    return {"kernel": "stream_read_kernel", "bytes": nb, "buffers": copies, "us": round(per * 1e6, 3),
+            "GB/s": round(nb / per / 1e9, 1), "frac_of_peak": round(nb / per / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def decode_figures(reps, args, per_step_time, n_steps):
+    """Per-step figures of a decode configuration from its median window."""
     R = len(reps)
+    kv = sum(reps[i % R].kv_bytes for i in range(n_steps)) / n_steps
+    seqs = sum(reps[i % R].batch for i in range(n_steps)) / n_steps
+    gbs = kv / per_step_time / 1e9
+    return kv, seqs, gbs
 
-    def capture(n, start):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                fn_per_step(reps[(start + i) % R])
-        return g
 
-    per = max(1, min(steps_per_graph, steps))
-    per = max(R, (per // R) * R)          # whole rotations inside a graph
-    g_full = capture(per, 0)
-    rem = steps % per
-    g_rem = capture(rem, 0) if rem else None
+def measure_other(W, dev, workload, min_seconds):
+    """One of the other decode configurations, in its default mode and split
+    plan: one replica (each reads 0.6-1.7 GB of KV per step, far past the
+    Infinity Cache), the step timed in windows like the headline one."""
+    import torch
+    mode = DEFAULT_MODES[workload]
+    mts = WORKLOADS[workload][2]
+    t0 = time.time()
+    reps = build_replicas(W, dev, workload, 1, mts, 32, mode, True)
     torch.cuda.synchronize()
-    for _ in range(max(1, warmup // per)):
-        g_full.replay()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps // per):
-        g_full.replay()
-    if g_rem is not None:
-        g_rem.replay()
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3
+    log(f"  built {workload} in {time.time() - t0:.1f}s")
+    check_replays_against_eager(reps, lambda r: r.step_once(), 4, 4)
+    steps = 64
+    sec, nwin, _ = time_windows(lambda r: r.step_once(), reps, steps, 16, 16, min_seconds)
+    per = sec / steps
+    kv, seqs, gbs = decode_figures(reps, None, per, steps)
+    r = reps[0]
+    res = {
+        "config": WORKLOADS[workload][3]["workload"],
+        "decode_mode": mode,
+        "max_tokens_per_split": None if mode == "balanced" else mts,
+        "append": "in the decode pass" if r.fused else "separate reshape_and_cache launch",
+        "kv_dtype": r.step.kv_dtype,
+        "batch": r.batch,
+        "kv_bytes_per_step": int(kv),
+        "us_per_step": round(per * 1e6, 2),
+        "GB/s": round(gbs, 1),
+        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "seq_steps_per_s": round(seqs / per, 1),
+        "windows": nwin,
+    }
+    res["stream_ceiling"] = stream_reference(int(kv), min_seconds)
+    res["frac_of_stream"] = round(gbs / res["stream_ceiling"]["GB/s"], 4)
+    del reps
+    torch.cuda.empty_cache()
+    return res
 
 
 def chunked_flops(step) -> int:
@@ -296,7 +433,48 @@ def chunked_flops(step) -> int:
     return total * step.num_q_heads * 4 * step.head_dim
 
 
-def measure_chunked(dev, iters: int = 200, kv_dtype: str = "i8"):
+def _dt(a, kind, dev):
+    import numpy as np
+    import torch
+    if kind == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def timed_graph(fn, calls_per_graph, min_seconds, check=None):
+    """Median seconds per call of ``fn`` replayed from a graph of
+    ``calls_per_graph`` calls, in windows of one replay, until min_seconds."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ref = check() if check else None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls_per_graph):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    if check is not None and not all(torch.equal(a, b) for a, b in zip(check(), ref)):
+        raise RuntimeError("the graph replay differs from the eager call")
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    nwin = max(WINDOWS_MIN, math.ceil(min_seconds / max(a.elapsed_time(b) / 1e3, 1e-7)))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nwin + 1)]
+    ev[0].record()
+    for i in range(nwin):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    secs = sorted(ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(nwin))
+    return secs[nwin // 2] / calls_per_graph, nwin
+
+
+def measure_chunked(dev, min_seconds, kv_dtype: str = "i8"):
     """The mixed int8 (or fp8) step: 4 x 512-row causal chunks over a
     1536-token cached prefix plus 124 decode rows. Times the chunked (MFMA)
     pass alone, and the whole step (cache write of 2172 rows, chunked pass,
@@ -307,27 +485,21 @@ def measure_chunked(dev, iters: int = 200, kv_dtype: str = "i8"):
     import paged_kv_attention_19_amd as pkv
     import workloads as W
     step = W.mixed_int8(kv_dtype=kv_dtype, max_tokens_per_split=MIXED_SPLIT)
-
-    def dt(a, kind):
-        if kind == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
     cache = pkv.KVCache.allocate(step.num_blocks, 8, 128, {"i8": pkv.I8, "fp8": pkv.FP8}[kv_dtype], dev)
-    pkv.reshape_and_cache(dt(step.prefix_k, "bf16"), dt(step.prefix_v, "bf16"),
-                          dt(step.prefix_slots.astype(np.int64), "i64"), cache)
-    new_k, new_v = dt(step.new_k, "bf16"), dt(step.new_v, "bf16")
-    new_s = dt(step.new_slots.astype(np.int64), "i64")
+    pkv.reshape_and_cache(_dt(step.prefix_k, "bf16", dev), _dt(step.prefix_v, "bf16", dev),
+                          _dt(step.prefix_slots.astype(np.int64), "i64", dev), cache)
+    new_k, new_v = _dt(step.new_k, "bf16", dev), _dt(step.new_v, "bf16", dev)
+    new_s = _dt(step.new_slots.astype(np.int64), "i64", dev)
     # the step's new rows (the chunks' own K/V and the decode tokens) are in the
     # cache before any pass reads it; the whole-step timing writes them again
     # (the same bytes)
     pkv.reshape_and_cache(new_k, new_v, new_s, cache)
-    qc, cu, tc, cc = step.chunk_batch()
-    qc, cu, tc, cc = dt(qc, "bf16"), dt(cu, "i32"), dt(tc, "i32"), dt(cc, "i32")
-    max_q = int(np.diff(step.chunk_batch()[1]).max())
+    qc_h, cu_h, tc_h, cc_h = step.chunk_batch()
+    qc, cu, tc, cc = _dt(qc_h, "bf16", dev), _dt(cu_h, "i32", dev), _dt(tc_h, "i32", dev), _dt(cc_h, "i32", dev)
+    max_q = int(np.diff(cu_h).max())
     qd, td, ctxd, nsd = step.decode_batch()
     max_ns = int(nsd.max())   # the decode rows: ceil(n / MIXED_SPLIT) splits each
-    qd, td, ctxd, nsd = dt(qd, "bf16"), dt(td, "i32"), dt(ctxd, "i32"), dt(nsd, "i32")
+    qd, td, ctxd, nsd = _dt(qd, "bf16", dev), _dt(td, "i32", dev), _dt(ctxd, "i32", dev), _dt(nsd, "i32", dev)
     out_c = torch.empty((qc.shape[0], 16, 128), dtype=torch.float32, device=dev)
     out_d = torch.empty((qd.shape[0], 16, 128), dtype=torch.float32, device=dev)
     ws = torch.zeros(max(256, pkv.decode_workspace_bytes(qd.shape[0], 16, 128, max_ns)), dtype=torch.uint8, device=dev)
@@ -341,72 +513,158 @@ def measure_chunked(dev, iters: int = 200, kv_dtype: str = "i8"):
         chunked()
         pkv.paged_attention_decode(qd, cache, td, ctxd, nsd, max_ns, scale, out=out_d, workspace=ws)
 
-    res = {}
-    for name, fn in (("chunked", chunked), ("step", whole)):
-        fn()
-        torch.cuda.synchronize()
-        eager = (out_c.clone(), out_d.clone())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(20):
-                fn()
-        g.replay()
-        torch.cuda.synchronize()
-        # the replayed graph must reproduce the eager call bit for bit (and a
-        # NaN, from a pool row never written, fails the comparison)
-        if not torch.equal(out_c, eager[0]) or (name == "step" and not torch.equal(out_d, eager[1])):
-            raise RuntimeError(f"the {name} graph replay differs from the eager call")
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(max(1, iters // 20)):
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        res[name] = a.elapsed_time(b) / 1e3 / (max(1, iters // 20) * 20)
+    t_chunked, nwin = timed_graph(chunked, 20, min_seconds, check=lambda: (out_c.clone(),))
+    t_step, _ = timed_graph(whole, 20, min_seconds, check=lambda: (out_c.clone(), out_d.clone()))
     flops = chunked_flops(step)
-    tflops = flops / res["chunked"] / 1e12
+    tflops = flops / t_chunked / 1e12
     kv_name = {"i8": "int8", "fp8": "fp8"}[kv_dtype]
+    prof = profile_figures(CHUNKED_PROFILE, CHUNKED_FILES, kv_dtype=kv_dtype)
     return {
         "workload": f"4 x 512-row causal chunks over 1536-token {kv_name} prefixes (16q/8kv/128), "
                     f"plus 124 {kv_name} decode rows in the whole step",
         "kernel": "chunked_kernel",
-        "chunked_us": round(res["chunked"] * 1e6, 3),
+        "chunked_us": round(t_chunked * 1e6, 3),
         "algorithmic_gflop": round(flops / 1e9, 3),
         "tflops": round(tflops, 2),
         "mfma_util": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-        "whole_step_us": round(res["step"] * 1e6, 3),
+        "whole_step_us": round(t_step * 1e6, 3),
+        "windows": nwin,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": prof.get("hbm_bytes_per_launch") if prof else None,
+            "trace_us": prof.get("kernel_trace_us") if prof else None,
+        },
     }
 
 
-def cpu_baseline(step, seconds):
-    """The oracle as it stands, on the host: decode sequences of the step one at
-    a time (gather through the block table + float64 attention for every query
-    head), cycling through the batch for about ``seconds``."""
-    from threadpoolctl import threadpool_limits
+def measure_spec_verify(dev, min_seconds):
+    """Speculative verification: 32 sequences, each checking 4 draft rows at
+    positions n - 4 .. n - 1 over its paged history (n uniform in [128, 384],
+    the Qwen3 heads, bf16), through the chunked entry point whose offset-causal
+    mask is the verification rule. 16 replicas (layers) are rotated so the KV
+    comes from HBM; reported as KV GB/s like the decode."""
+    import numpy as np
+    import torch
 
+    import paged_kv_attention_19_amd as pkv
+    import workloads as W
+    reps = []
+    for r in range(16):
+        rng = np.random.default_rng(np.random.SeedSequence([1906, 7]))
+        ctx = rng.integers(128, 384, size=32, endpoint=True)
+        step = W.make_step("spec_verify", ctx, np.full(32, 4), num_q_heads=16, num_kv_heads=8, head_dim=128,
+                           num_blocks=4096, seed=1906, values_seed=1906 + 1000 * r)
+        cache = pkv.KVCache.allocate(step.num_blocks, 8, 128, pkv.BF16, dev)
+        for k, v, s in ((step.prefix_k, step.prefix_v, step.prefix_slots), (step.new_k, step.new_v, step.new_slots)):
+            pkv.reshape_and_cache(_dt(k, "bf16", dev), _dt(v, "bf16", dev), _dt(s.astype(np.int64), "i64", dev), cache)
+        q, cu, tab, cc = step.chunk_batch()
+        reps.append(dict(q=_dt(q, "bf16", dev), cu=_dt(cu, "i32", dev), tab=_dt(tab, "i32", dev),
+                         ctx=_dt(cc, "i32", dev), cache=cache, scale=float(step.scale),
+                         out=torch.empty((q.shape[0], 16, 128), dtype=torch.float32, device=dev),
+                         kv=int(cc.sum()) * kv_bytes_per_token(8, 128, 2)))
+
+    def call(r):
+        pkv.paged_attention_chunked(r["q"], r["cu"], 4, r["cache"], r["tab"], r["ctx"], r["scale"], out=r["out"])
+
+    steps = 512
+    sec, nwin, _ = time_windows(call, reps, steps, 256, 64, min_seconds)
+    per = sec / steps
+    kv = sum(r["kv"] for r in reps) / len(reps)
+    return {"config": "spec_verify_b32_q4", "entry_point": "pkv_paged_attention_chunked", "kernel": "chunked_kernel",
+            "rows_per_seq": 4, "context_lens": "uniform[128,384]", "kv_bytes_per_step": int(kv),
+            "us_per_step": round(per * 1e6, 2), "GB/s": round(kv / per / 1e9, 1),
+            "hbm_peak_frac": round(kv / per / 1e9 / HBM_PEAK_GBS, 4), "seq_steps_per_s": round(32 / per, 1),
+            "windows": nwin}
+
+
+# ---------------------------------------------------------------------------
+# the oracle on the host (run before the GPU is touched: the all-core timing
+# forks worker processes, which must not inherit an initialised GPU runtime)
+# ---------------------------------------------------------------------------
+
+_CPU = {}
+
+
+def _cpu_setup(step):
     import oracle
     pool = oracle.OraclePool(step.num_blocks, step.num_kv_heads, step.block_size, step.head_dim, step.kv_dtype)
     oracle.reshape_and_cache(pool, step.prefix_k, step.prefix_v, step.src_dtype, step.prefix_slots)
     oracle.reshape_and_cache(pool, step.new_k, step.new_v, step.src_dtype, step.new_slots)
     q, tables, ctx, _ = step.decode_batch()
-    q64 = oracle.decode_rows(q, step.q_dtype)
     eb, sb = {"f32": (4, 0), "bf16": (2, 0), "i8": (1, 4), "fp8": (1, 4)}[step.kv_dtype]
-    per_tok = kv_bytes_per_token(step.num_kv_heads, step.head_dim, eb, sb)
-    done_bytes = 0
-    seqs = 0
+    _CPU.update(pool=pool, q64=oracle.decode_rows(q, step.q_dtype), tables=tables, ctx=ctx, scale=step.scale,
+                per_tok=kv_bytes_per_token(step.num_kv_heads, step.head_dim, eb, sb))
+
+
+def _cpu_worker(args):
+    """Decode sequences start, start + stride, ... (cycling) for `seconds`
+    with BLAS on one thread; returns (KV bytes, sequences, seconds)."""
+    start, stride, seconds = args
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    c = _CPU
+    done = seqs = 0
+    B = len(c["ctx"])
     with threadpool_limits(1):
         t0 = time.perf_counter()
+        b = start
         while True:
-            b = seqs % len(ctx)
-            oracle.paged_decode(q64[b:b + 1], pool, tables[b:b + 1], ctx[b:b + 1], step.scale)
-            done_bytes += int(ctx[b]) * per_tok
+            i = b % B
+            oracle.paged_decode(c["q64"][i:i + 1], c["pool"], c["tables"][i:i + 1], c["ctx"][i:i + 1], c["scale"])
+            done += int(c["ctx"][i]) * c["per_tok"]
             seqs += 1
+            b += stride
             el = time.perf_counter() - t0
             if el >= seconds:
-                break
-    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{seqs} sequence decodes ({min(seqs, len(ctx))} distinct of the step's {len(ctx)}; "
-                      f"{done_bytes / 1e6:.1f} MB of KV) in {el:.1f} s, float64 NumPy, BLAS limited to 1 thread"}
+                return done, seqs, el
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(step, seconds):
+    """The oracle as it stands, on the host: decode sequences of the step one at
+    a time (gather through the block table + float64 attention for every query
+    head), on one core, then on every core the process may use (at most 16) in
+    worker processes, each on its own share of the batch."""
+    import multiprocessing as mp
+    _cpu_setup(step)
+    B = len(_CPU["ctx"])
+    done, seqs, el = _cpu_worker((0, 1, seconds))
+    one = {"value": round(done / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{seqs} sequence decodes ({min(seqs, B)} distinct of the step's {B}; "
+                     f"{done / 1e6:.1f} MB of KV) in {el:.1f} s, float64 NumPy, BLAS on 1 thread"}
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:   # pragma: no cover
+        avail = os.cpu_count() or 1
+    n = max(1, min(16, avail))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(n) as pool:
+        res = pool.map(_cpu_worker, [(i, n, seconds) for i in range(n)])
+    wall = time.perf_counter() - t0
+    done_all = sum(r[0] for r in res)
+    seqs_all = sum(r[1] for r in res)
+    one["all_cores"] = {"value": round(done_all / wall / 1e9, 4), "unit": "GB/s", "cores": n,
+                        "sample": f"{seqs_all} sequence decodes ({done_all / 1e6:.1f} MB of KV) over {n} worker "
+                                  f"processes (one per core, BLAS on 1 thread each) in {wall:.1f} s of wall time"}
+    one["cpu_model"] = cpu_model()
+    one["cpus_visible"] = avail
+    return one
 
 
 def main():
@@ -422,16 +680,7 @@ def main():
         copy_calibration(args.copy_calibration)
         return
 
-    import torch
-
-    import paged_kv_attention_19_amd as pkv
     import workloads as W
-
-    if not torch.cuda.is_available():
-        log("no GPU visible")
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    pkv.lib()
     build, default_reps, default_mts, cfg_text = WORKLOADS[args.workload]
     if args.decode_mode is None:
         args.decode_mode = DEFAULT_MODES[args.workload]
@@ -439,65 +688,56 @@ def main():
         args.max_tokens_per_split = default_mts
     if args.replicas is None:
         args.replicas = default_reps
-    seed0 = DEFAULT_SEEDS[args.workload] if args.seed is None else args.seed
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        seed0 = DEFAULT_SEEDS[args.workload] if args.seed is None else args.seed
+        cpu = cpu_baseline(build(W, seed0, args.max_tokens_per_split, args.batch, 0), args.cpu_seconds)
+
+    import torch
+
+    import paged_kv_attention_19_amd as pkv
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    pkv.lib()
     t0 = time.time()
-    reps = []
-    for r in range(args.replicas):
-        step = build(W, seed0, args.max_tokens_per_split, args.batch, r)
-        reps.append(Replica(step, dev, args.max_tokens_per_split, balanced=args.decode_mode == "balanced",
-                            fuse=not args.no_fuse))
+    reps = build_replicas(W, dev, args.workload, args.replicas, args.max_tokens_per_split, args.batch,
+                          args.decode_mode, not args.no_fuse, seed=args.seed)
     torch.cuda.synchronize()
     log(f"built {len(reps)} replicas in {time.time() - t0:.1f}s; max_ns={[r.max_ns for r in reps][:4]}...")
-
-    # eager reference of one step per replica, then check graph replays against it
-    eager = []
-    for r in reps:
-        r.step_once()
-    torch.cuda.synchronize()
-    for r in reps:
-        eager.append((r.out.clone(), r.lse.clone()))
-        r.out.fill_(float("nan"))
-        r.lse.fill_(float("nan"))
+    check_replays_against_eager(reps, lambda r: r.step_once(), args.steps, args.steps_per_graph)
 
     steps = args.steps
-    sec = time_graphs(lambda r: r.step_once(), reps, steps, args.steps_per_graph, args.warmup)
-    for r, (eo, el) in zip(reps, eager):
-        if not (torch.equal(r.out, eo) and torch.equal(r.lse, el)):
-            log("graph replay output differs from the eager step")
-            sys.exit(1)
+    sec, nwin, timed = time_windows(lambda r: r.step_once(), reps, steps, args.steps_per_graph, args.warmup,
+                                    args.min_seconds)
+    per_step = sec / steps
     R = len(reps)
-    kv_total = sum(reps[i % R].kv_bytes for i in range(steps))
-    seqs_total = sum(reps[i % R].batch for i in range(steps))
-    value = kv_total / sec / 1e9
+    kv_step, seqs_step, value = decode_figures(reps, args, per_step, steps)
 
-    # per-kernel launch durations: graphs holding one kind of launch
+    # per-kernel launch durations: graphs holding one kind of launch, timed
+    # in windows the same way
     per_kernel = {}
     n_k = min(steps, 4096)
-    sec_p = time_graphs(lambda r: r.partials(), reps, n_k, args.steps_per_graph, 64)
     fused = reps[0].fused
     dom = "decode_balanced" if reps[0].balanced else ("decode_append" if fused else "decode_partial")
-    per_kernel[dom] = sec_p / n_k
+    sp, _, _ = time_windows(lambda r: r.partials(), reps, n_k, args.steps_per_graph, 64, args.min_seconds)
+    per_kernel[dom] = sp / n_k
     if reps[0].max_ns > 1:
-        sec_c = time_graphs(lambda r: r.combine(), reps, n_k, args.steps_per_graph, 64)
-        per_kernel["lse_combine"] = sec_c / n_k
-    sec_r = time_graphs(lambda r: r.reshape(), reps, n_k, args.steps_per_graph, 64)
-    per_kernel["reshape_and_cache"] = sec_r / n_k
+        sc, _, _ = time_windows(lambda r: r.combine(), reps, n_k, args.steps_per_graph, 64, args.min_seconds)
+        per_kernel["lse_combine"] = sc / n_k
+    sr, _, _ = time_windows(lambda r: r.reshape(), reps, n_k, args.steps_per_graph, 64, args.min_seconds)
+    per_kernel["reshape_and_cache"] = sr / n_k
     partial_bytes = sum(reps[i % R].kv_bytes for i in range(n_k)) / n_k
     # algorithmic bytes of the dominant launch: the KV it reads, plus, when it
     # appends, the new rows it reads and writes
     launch_bytes = partial_bytes + (sum(reps[i % R].append_bytes for i in range(n_k)) / n_k if fused else 0)
     achieved = launch_bytes / per_kernel[dom] / 1e9
-
-    traffic = None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if (tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == args.workload
-                and tr.get("decode_mode") == args.decode_mode and tr.get("append") == fused
-                and tr.get("max_tokens_per_split") == args.max_tokens_per_split):
-            traffic = tr.get("hbm_bytes_per_launch")
-    except (OSError, ValueError):
-        pass
+    prof = profile_figures(DECODE_PROFILE, DECODE_FILES, workload=args.workload, decode_mode=args.decode_mode,
+                           append=fused, max_tokens_per_split=args.max_tokens_per_split)
+    trace_us = prof.get("kernel_trace_us") if prof else None
 
     line = {
         "metric": METRIC,
@@ -506,7 +746,7 @@ def main():
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,
-        "ms_per_step": round(sec / steps * 1e3, 6),
+        "ms_per_step": round(per_step * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -519,11 +759,12 @@ def main():
             "decode_mode": args.decode_mode,
             "append": "in the decode pass" if fused else "separate reshape_and_cache launch",
             "max_tokens_per_split": None if reps[0].balanced else args.max_tokens_per_split,
-            "replicas": R, "kv_bytes_per_step": int(kv_total / steps),
+            "replicas": R, "kv_bytes_per_step": int(kv_step),
             "parallelism": "none",
         }),
+        "timing": {"steps_per_window": steps, "windows": nwin, "stat": "median window", "timed_s": round(timed, 3)},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
-        "seq_steps_per_s": round(seqs_total / sec, 1),
+        "seq_steps_per_s": round(seqs_step / per_step, 1),
         "kernel_us": {k: round(v * 1e6, 3) for k, v in per_kernel.items()},
         "roofline": {
             "bound": "hbm",
@@ -533,16 +774,32 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
+            "traffic": prof.get("hbm_bytes_per_launch") if prof else None,
+            "trace_us": trace_us,
+            "trace_frac": round(launch_bytes / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if trace_us else None,
         },
     }
-    line["copy_reference"] = copy_reference(int(partial_bytes))
+    del reps
+    torch.cuda.empty_cache()
+    log("timing the read-only stream ceiling ...")
+    line["stream_ceiling"] = stream_reference(int(partial_bytes), args.min_seconds)
+    line["frac_of_stream"] = round(value / line["stream_ceiling"]["GB/s"], 4)
+    line["roofline"]["frac_of_stream"] = round(achieved / line["stream_ceiling"]["GB/s"], 4)
     if not args.no_chunked:
         log("timing the chunked prefill ...")
-        line["chunked_prefill"] = measure_chunked(dev, kv_dtype=args.chunked_kv)
-    if not args.no_cpu_baseline:
-        log("timing the oracle on the host ...")
-        line["cpu_baseline"] = cpu_baseline(reps[0].step, args.cpu_seconds)
+        line["chunked_prefill"] = measure_chunked(dev, args.min_seconds, kv_dtype=args.chunked_kv)
+    if not args.no_others:
+        line["other_configs"] = {}
+        for wl in OTHER_CONFIGS:
+            if wl == args.workload:
+                continue
+            log(f"timing {wl} ...")
+            r = measure_other(W, dev, wl, args.min_seconds)
+            line["other_configs"][r.pop("config")] = r
+        log("timing the speculative-verify shape ...")
+        line["spec_verify"] = measure_spec_verify(dev, args.min_seconds)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
