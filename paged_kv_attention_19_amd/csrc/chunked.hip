@@ -532,7 +532,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
       for (int e = 0; e < 4; ++e) {
         const int v = 4 * c + e;
         float x = sv[v];
-        if constexpr (kScaled) x *= kv[e];   // K scale x softmax scale
+        if constexpr (kScaled) {
+          // K scale x softmax scale, rounded here: the max below and the
+          // exponent's argument must use the same value. (Contracted into the
+          // later subtraction, the product would enter the exponent
+          // unrounded, and the largest weight would miss its exact power of
+          // two by a few ulps.)
+#pragma clang fp contract(off)
+          x *= kv[e];
+        }
         if constexpr (kDiag) {
           if (tok_of(v) > tlim) x = neg_inf();
         }
