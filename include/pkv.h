@@ -187,6 +187,42 @@ pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t ba
                                       void* stream);
 
 /*
+ * paged_attention_decode_noalloc: pkv_paged_attention_decode for callers that
+ * cannot allocate device memory -- code under HIP graph capture, serving loops
+ * that must not allocate, harnesses that forbid hipMalloc. The call allocates
+ * nothing and takes no workspace: the split partials, or the balanced mode's
+ * counters and partial slots, live in a fixed device array of
+ * PKV_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.
+ *   Arguments : as pkv_paged_attention_decode without the workspace; `out`
+ *               must not be NULL (no partials-only mode).
+ *   Limit     : the scratch a call needs must fit the array:
+ *                 max_num_splits == 1 : none;
+ *                 max_num_splits  > 1 : batch * max_num_splits * num_q_heads *
+ *                                       (head_dim + 1) * 4 bytes (rounded up to 256);
+ *                 max_num_splits == 0 : batch * num_q_heads * 4 (rounded up to
+ *                                       256) + 2048 * 2 * (num_q_heads /
+ *                                       num_kv_heads) * (head_dim + 1) * 4 bytes.
+ *               A larger call returns PKV_ERR_WORKSPACE and launches nothing.
+ *   Sharing   : every call on one GPU uses that GPU's one array. Calls that
+ *               overlap on one GPU (different streams, or different threads
+ *               without ordering) race and give undefined results; calls on
+ *               one stream are fine. The balanced mode clears its counters
+ *               at the start of each call (a small extra launch).
+ *   Set-up    : the first call on a device looks up the array's device
+ *               address there (that device must be current); a failure
+ *               returns PKV_ERR_HIP.
+ * Results equal pkv_paged_attention_decode's bit for bit (the same kernels).
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (((size_t)48) << 20)
+pkv_status pkv_paged_attention_decode_noalloc(const void* q, int32_t q_dtype, int32_t batch,
+                                              int32_t num_q_heads, const pkv_cache* cache,
+                                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                              const int32_t* context_lens, const int32_t* num_splits,
+                                              int32_t max_num_splits, float scale, float* out,
+                                              float* out_lse, void* stream);
+
+/*
  * paged_attention_decode_append: pkv_reshape_and_cache of the step's new
  * rows followed by pkv_paged_attention_decode, in one pass (page
  * "llm-inference" on shehab-ashraf.github.io, section "KV Cache", subsection

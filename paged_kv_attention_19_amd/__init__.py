@@ -25,11 +25,12 @@ import torch
 __all__ = [
     "F32", "BF16", "I8", "FP8", "PkvError", "KVCache", "lib", "library_path", "exported_symbols",
     "reshape_and_cache", "decode_workspace_bytes", "decode_default_max_num_splits", "paged_attention_decode",
-    "paged_attention_decode_append", "paged_attention_chunked", "lse_combine",
-    "version", "stream_read",
+    "paged_attention_decode_append", "paged_attention_decode_noalloc", "paged_attention_chunked", "lse_combine",
+    "version", "NOALLOC_SCRATCH_BYTES", "stream_read",
 ]
 
 F32, BF16, I8, FP8 = 0, 1, 2, 3
+NOALLOC_SCRATCH_BYTES = 48 << 20   # PKV_NOALLOC_SCRATCH_BYTES of the C header
 _TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8, FP8: torch.float8_e4m3fn}
 _CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.float8_e4m3fn: FP8}
 _SCALED = (I8, FP8)   # 8-bit codes with a float32 scale per (token, kv head)
@@ -75,6 +76,8 @@ _SIGS = {
                                     ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], _I32),
     "pkv_paged_attention_decode_append": ([_P, _P, _I32, _P, _P, _I32, _I32, _I32, ctypes.POINTER(_Cache), _P, _I32,
                                            _P, _P, _I32, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], _I32),
+    "pkv_paged_attention_decode_noalloc": ([_P, _I32, _I32, _I32, ctypes.POINTER(_Cache), _P, _I32, _P, _P, _I32,
+                                            ctypes.c_float, _P, _P, _P], _I32),
     "pkv_paged_attention_chunked": ([_P, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Cache), _P, _I32, _P,
                                      ctypes.c_float, _P, _P, _P], _I32),
     "pkv_lse_combine": ([_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
@@ -378,6 +381,24 @@ def paged_attention_decode_append(k_new: torch.Tensor, v_new: torch.Tensor, slot
         n_o = B * max_num_splits * Hq * D
         return (f[:n_o].view(B, max_num_splits, Hq, D),
                 f[n_o:n_o + B * max_num_splits * Hq].view(B, max_num_splits, Hq))
+    return (out, out_lse) if (return_lse or out_lse is not None) else out
+
+
+def paged_attention_decode_noalloc(q: torch.Tensor, cache: KVCache, block_tables: torch.Tensor,
+                                   context_lens: torch.Tensor, num_splits: torch.Tensor | None,
+                                   max_num_splits: int, scale: float, out: torch.Tensor | None = None,
+                                   out_lse: torch.Tensor | None = None, return_lse: bool = False):
+    """:func:`paged_attention_decode` without a workspace: the library keeps
+    the partials in its own fixed device array (``NOALLOC_SCRATCH_BYTES`` per
+    GPU), for callers that cannot allocate. Pass ``out`` (and ``out_lse``) to
+    allocate nothing here either. Calls that overlap on one GPU race."""
+    B, Hq, D = _check_decode_inputs(q, cache, block_tables, context_lens, num_splits)
+    out, out_lse = _check_out(out, out_lse, B, Hq, D, q.device, return_lse)
+    d = cache.descriptor()
+    _check(lib().pkv_paged_attention_decode_noalloc(
+        q.data_ptr(), _CODE[q.dtype], B, Hq, ctypes.byref(d), block_tables.data_ptr(), block_tables.shape[1],
+        context_lens.data_ptr(), _ptr(num_splits), int(max_num_splits), float(scale), out.data_ptr(),
+        _ptr(out_lse), _stream_handle()))
     return (out, out_lse) if (return_lse or out_lse is not None) else out
 
 

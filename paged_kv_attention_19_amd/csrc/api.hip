@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 
 #include "pkv.h"
@@ -116,6 +117,56 @@ int balanced_workgroups(int batch, int num_kv_heads, int max_blocks) {
 
 }  // namespace
 
+// ---- scratch memory of the allocation-free decode entry point ----
+// One fixed device array per GPU the library runs on, held until the process
+// ends. Host code never uses the array's name as an address (on the host it
+// is only a stand-in for the symbol): it asks the runtime for the device
+// address once per device and passes that to the kernels.
+constexpr size_t kScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Zero n int32 words (the balanced mode's arrival counters). A kernel rather
+// than a memset node, so that a captured graph replays it correctly.
+__global__ void zero_words_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there (with that device current) and kept.
+pkv_status scratch_address(const char* fn, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_UNSUPPORTED, "%s: device %d (built: < %d)", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(PKV_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed: %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+// Scratch bytes the no-alloc decode needs: as pkv_decode_workspace_bytes,
+// but with the balanced mode's partial slots sized for the actual GQA group.
+size_t noalloc_bytes(int batch, int num_q_heads, int group, int head_dim, int max_num_splits) {
+  if (max_num_splits == 0) return balanced_counter_bytes(batch, num_q_heads) + balanced_part_bytes(group, head_dim);
+  return pkv_decode_workspace_bytes(batch, num_q_heads, head_dim, max_num_splits);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* pkv_last_error(void) { return g_error.c_str(); }
@@ -174,7 +225,7 @@ static pkv_status check_decode(const char* fn, const void* q, int32_t q_dtype, i
                                const pkv_cache* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                                const int32_t* context_lens, const int32_t* num_splits, int32_t max_num_splits,
                                float scale, const float* out, const void* workspace, size_t workspace_bytes,
-                               bool* empty) {
+                               bool* empty, bool library_scratch = false) {
   if (pkv_status st = check_cache(cache, fn); st != PKV_OK) return st;
   if (batch < 0) return fail(PKV_ERR_INVALID_ARG, "%s: batch=%d", fn, batch);
   if (pkv_status st = check_group(num_q_heads, cache->num_kv_heads, fn); st != PKV_OK) return st;
@@ -203,7 +254,7 @@ static pkv_status check_decode(const char* fn, const void* q, int32_t q_dtype, i
     return fail(PKV_ERR_UNSUPPORTED, "%s: batch too large for the balanced mode", fn);
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "%s: scale is not finite", fn);
   const int D = cache->head_dim;
-  const size_t need = pkv_decode_workspace_bytes(batch, num_q_heads, D, max_num_splits);
+  const size_t need = library_scratch ? 0 : pkv_decode_workspace_bytes(batch, num_q_heads, D, max_num_splits);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace == nullptr ? size_t(0) : workspace_bytes);
@@ -475,6 +526,45 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
   if (e == hipErrorNotSupported) return fail(PKV_ERR_UNSUPPORTED, "%s: this configuration is not built", fn);
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
+}
+
+pkv_status pkv_paged_attention_decode_noalloc(const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                              const pkv_cache* cache, const int32_t* block_tables,
+                                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                              const int32_t* num_splits, int32_t max_num_splits, float scale,
+                                              float* out, float* out_lse, void* stream) {
+  const char* fn = "pkv_paged_attention_decode_noalloc";
+  if (out == nullptr) return fail(PKV_ERR_INVALID_ARG, "%s: out is NULL (no partials-only mode here)", fn);
+  // every argument is checked as for pkv_paged_attention_decode; the
+  // library's scratch stands in for the workspace
+  bool empty = false;
+  if (pkv_status st = check_decode(fn, q, q_dtype, batch, num_q_heads, cache, block_tables, max_blocks_per_seq,
+                                   context_lens, num_splits, max_num_splits, scale, out, nullptr, 0, &empty,
+                                   /*library_scratch=*/true);
+      st != PKV_OK || empty)
+    return st;
+  const int group = num_q_heads / cache->num_kv_heads;
+  const size_t need = noalloc_bytes(batch, num_q_heads, group, cache->head_dim, max_num_splits);
+  if (need > kScratchBytes)
+    return fail(PKV_ERR_WORKSPACE, "%s: needs %zu bytes of scratch, the library holds %zu per device "
+                "(fewer splits or a smaller batch per call, or pkv_paged_attention_decode with a workspace)",
+                fn, need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    if (pkv_status st = scratch_address(fn, &ws); st != PKV_OK) return st;
+  }
+  if (max_num_splits == 0) {
+    // the array keeps the last call's contents (another mode's partials may
+    // sit where the counters go): clear the counters first
+    const int words = static_cast<int>(balanced_counter_bytes(batch, num_q_heads) / sizeof(int32_t));
+    hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<int32_t*>(ws), words);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, fn);
+    return run_balanced_decode(fn, q, q_dtype, batch, num_q_heads, cache, block_tables, max_blocks_per_seq,
+                               context_lens, scale, out, out_lse, ws, stream);
+  }
+  return run_split_decode(fn, q, q_dtype, batch, num_q_heads, cache, block_tables, max_blocks_per_seq, context_lens,
+                          num_splits, max_num_splits, scale, out, out_lse, ws, nullptr, stream);
 }
 
 }  // extern "C"

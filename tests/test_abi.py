@@ -160,6 +160,33 @@ def test_binding_refuses_cpu_tensors():
         pkv.paged_attention_decode(q, None, q, q, None, 1, 0.1)
 
 
+def test_noalloc_decode_rejects_before_any_device_call():
+    """The allocation-free decode checks its arguments like the workspace
+    decode, then refuses a call whose scratch would not fit the library's
+    fixed array (PKV_ERR_WORKSPACE), all before touching the device."""
+    L = pkv.lib()
+
+    def na(c, **kw):
+        a = dict(batch=3, hq=4, maxb=4, ns=FAKE, max_ns=2, out=FAKE)
+        a.update(kw)
+        return L.pkv_paged_attention_decode_noalloc(FAKE, pkv.BF16, a["batch"], a["hq"], ctypes.byref(c), FAKE,
+                                                    a["maxb"], FAKE, a["ns"], a["max_ns"], 0.125, a["out"], None,
+                                                    None)
+
+    c = cache(head_dim=128)
+    assert na(c, out=None) == -1
+    assert na(c, ns=None) == -1
+    assert na(cache(block_size=32)) == -2
+    # 4096 x 64 splits x 4 heads x 129 floats = 541 MB > 48 MiB
+    assert na(c, batch=4096, max_ns=64) == -3
+    assert "needs" in L.pkv_last_error().decode()
+    # balanced, group of 8: 65535 x 128 q heads of counters (33.6 MB) + 2048 x 2 x 8 x 129 x 4 (16.9 MB)
+    # = 50.4 MB > 48 MiB
+    assert na(cache(head_dim=128, num_kv_heads=16), batch=65535, hq=128, ns=None, max_ns=0) == -3
+    assert na(c, batch=0) == 0
+    assert pkv.NOALLOC_SCRATCH_BYTES == 48 << 20
+
+
 def test_stream_read_rejects_bad_arguments():
     L = pkv.lib()
     assert L.pkv_stream_read(None, 1024, FAKE, None) == -1
