@@ -30,6 +30,19 @@
  *    max_blocks_per_seq * block_size, or a split count outside
  *    [1, max_num_splits] turns that sequence's outputs into NaN; a slot outside
  *    [0, num_blocks * block_size) is skipped like a negative slot.
+ *  - Debug mode: with the environment variable PKV_DEBUG=1 (read at every
+ *    call), the calls that read such values first run a validation pass over
+ *    them on `stream`, WAIT for it (a host synchronisation, so not usable under
+ *    graph capture), and return PKV_ERR_INVALID_ARG without launching the
+ *    computation if an entry is bad: a context length outside
+ *    [0, max_blocks_per_seq * block_size], a block id outside [0, num_blocks)
+ *    among a sequence's first ceil(n / block_size) entries, a split count
+ *    outside [1, max_num_splits], cu_q_lens[0] != 0, a decreasing cu_q_lens, a
+ *    chunk longer than max_q_len or than its context, a slot past the pool, or
+ *    (decode with append) a slot that is not the slot of token n - 1.
+ *    pkv_last_error() names the first offending entry. The validation's
+ *    finding lives in a fixed device word per GPU, so debug-mode calls that
+ *    overlap on one GPU may report each other's findings.
  *  - Launch failures reported by the HIP runtime return PKV_ERR_HIP.
  *  - Calls on one stream run in order; calls on different streams that write
  *    the same buffers race.
@@ -266,6 +279,11 @@ pkv_status pkv_paged_attention_decode_append(const void* k_new, const void* v_ne
  *                  [total_q][num_q_heads] or NULL (natural log).
  *   Cache dtypes: BF16, I8 or FP8; head_dim 128; GQA group size in {1, 2, 4, 8}.
  *   A chunk longer than max_q_len or than its context yields NaN rows.
+ * Chunks of a few rows -- max_q_len * (num_q_heads / num_kv_heads) <= 4,
+ * e.g. verification of 2 rows with 2 query heads per kv head -- run on the
+ * decode kernels: every chunk row of a kv head's query
+ * heads is scored against each K/V tile as it streams (exact products, fp32
+ * sums and weights, the decode's arithmetic). Longer chunks run on MFMA:
  * Arithmetic: QK^T with bf16 MFMA (exact products, fp32 sums); softmax in
  * fp32. The PV product's weights are bf16 pairs (a high part and its
  * residual, ~2^-17) over a BF16 cache, and fp16 (rounded once, 2^-12, with

@@ -36,6 +36,37 @@ pkv_status hip_fail(hipError_t e, const char* what) {
   return fail(PKV_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
 }
 
+// PKV_DEBUG=1: validate the device-resident metadata of a call before its
+// launches (a synchronising pass; see validate.hip). Returns PKV_OK when the
+// mode is off or nothing is wrong.
+pkv_status debug_validate(const char* fn, const pkv::DebugRequest& r, void* stream) {
+  if (!pkv::debug_enabled()) return PKV_OK;
+  pkv::DebugFinding f{};
+  const hipError_t e = pkv::debug_check(r, static_cast<hipStream_t>(stream), &f);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s: PKV_DEBUG validation did not run: %s", fn, hipGetErrorString(e));
+  if (f.code == 0) return PKV_OK;
+  char what[256];
+  snprintf(what, sizeof(what), pkv::debug_code_text(f.code), f.index);
+  return fail(PKV_ERR_INVALID_ARG, "%s: PKV_DEBUG: %s", fn, what);
+}
+
+// The decode calls' metadata, for debug_validate.
+pkv::DebugRequest decode_request(int32_t batch, const pkv_cache* cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* num_splits,
+                                 int32_t max_num_splits) {
+  pkv::DebugRequest r;
+  r.tables = block_tables;
+  r.max_blocks = max_blocks_per_seq;
+  r.ctx = context_lens;
+  r.batch = batch;
+  r.num_blocks = cache->num_blocks;
+  if (max_num_splits > 1) {   // one split per sequence and the balanced mode read no split counts
+    r.nsplits = num_splits;
+    r.max_ns = max_num_splits;
+  }
+  return r;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 const char* dtype_name(int d) {
@@ -103,6 +134,17 @@ int decode_waves(int /*max_blocks_per_seq*/, int /*max_num_splits*/) {
 // (pkv_decode_workspace_bytes knows only num_q_heads and sizes the slots for
 // a group of num_q_heads; the kernel uses group * (head_dim + 1) floats per
 // slot.)
+// Chunks of at most this many query rows per kv head (max_q_len times the GQA
+// group) go to the decode kernels rather than the MFMA kernel: with so few
+// rows a 128-row MFMA tile is mostly empty, while the decode kernels stream
+// the K/V tiles once with every row in registers. Their VALU work grows with
+// the rows, so past 4 rows the MFMA kernel is faster. Measured on MI355X, 32
+// sequences of 128..384 tokens (bf16, 8 kv heads), L new rows each with G
+// query heads per kv head, decode kernels against MFMA kernel: L x G = 1 or
+// 2: 9.9-10.1 against 18.0-18.8 us; 4: 13.0-13.2 against 18.1-18.8 us; 8:
+// 23.8-25.0 against 18.3-19.9 us.
+constexpr int kRowsDecodeMax = 4;
+
 constexpr int kBalancedMaxWorkgroups = 512;
 size_t balanced_part_bytes(int heads_per_slot, int head_dim) {
   return static_cast<size_t>(kBalancedMaxWorkgroups) * 4 * 2 * heads_per_slot * (head_dim + 1) * sizeof(float);
@@ -205,6 +247,11 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, int32_t s
   p.num_tokens = num_tokens;
   p.num_kv_heads = cache->num_kv_heads;
   p.num_slots = static_cast<int64_t>(cache->num_blocks) * cache->block_size;
+  pkv::DebugRequest dr;
+  dr.slots = slot_mapping;
+  dr.num_tokens = num_tokens;
+  dr.num_slots = p.num_slots;
+  if (pkv_status st = debug_validate(fn, dr, stream); st != PKV_OK) return st;
   const hipError_t e = pkv::launch_reshape(p, src_dtype, kv, cache->head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
@@ -413,6 +460,11 @@ pkv_status pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t ba
                                    &empty);
       st != PKV_OK || empty)
     return st;
+  if (pkv_status st = debug_validate(fn, decode_request(batch, cache, block_tables, max_blocks_per_seq, context_lens,
+                                                        num_splits, max_num_splits),
+                                     stream);
+      st != PKV_OK)
+    return st;
   if (max_num_splits == 0)
     return run_balanced_decode(fn, q, q_dtype, batch, num_q_heads, cache, block_tables, max_blocks_per_seq,
                                context_lens, scale, out, out_lse, workspace, stream);
@@ -450,6 +502,10 @@ pkv_status pkv_paged_attention_decode_append(const void* k_new, const void* v_ne
     return fail(PKV_ERR_INVALID_ARG, "%s: %s cache needs %s rows, got %s", fn, dtype_name(kv), dtype_name(kv),
                 dtype_name(src_dtype));
   }
+  pkv::DebugRequest dr =
+      decode_request(batch, cache, block_tables, max_blocks_per_seq, context_lens, num_splits, max_num_splits);
+  dr.append_slots = slot_mapping;
+  if (pkv_status st = debug_validate(fn, dr, stream); st != PKV_OK) return st;
   const AppendArgs append{k_new, v_new, src_dtype, slot_mapping};
   return run_split_decode(fn, q, q_dtype, batch, num_q_heads, cache, block_tables, max_blocks_per_seq, context_lens,
                           num_splits, max_num_splits, scale, out, out_lse, workspace, &append, stream);
@@ -478,6 +534,11 @@ pkv_status pkv_lse_combine(const float* o_part, const float* lse_part, int32_t b
   cp.batch = batch;
   cp.num_q_heads = num_q_heads;
   cp.max_ns = max_num_splits;
+  pkv::DebugRequest dr;
+  dr.nsplits = num_splits;
+  dr.max_ns = max_num_splits;
+  dr.batch = batch;
+  if (pkv_status st = debug_validate(fn, dr, stream); st != PKV_OK) return st;
   const hipError_t e = pkv::launch_combine(cp, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
@@ -521,6 +582,48 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
   p.num_blocks = cache->num_blocks;
   p.max_q_len = max_q_len;
   p.scale_log2 = scale * 1.4426950408889634f;
+  pkv::DebugRequest dr;
+  dr.tables = block_tables;
+  dr.max_blocks = max_blocks_per_seq;
+  dr.ctx = context_lens;
+  dr.batch = num_seqs;
+  dr.num_blocks = cache->num_blocks;
+  dr.cu_q = cu_q_lens;
+  dr.max_q_len = max_q_len;
+  if (pkv_status st = debug_validate(fn, dr, stream); st != PKV_OK) return st;
+  const int group = num_q_heads / cache->num_kv_heads;
+  if (static_cast<int64_t>(max_q_len) * group <= kRowsDecodeMax) {
+    // chunks of a few rows (speculative verification): the decode kernels,
+    // with every chunk row of a kv head's query heads on each K/V tile
+    pkv::DecodeParams dp{};
+    dp.q = q;
+    dp.k = cache->k;
+    dp.v = cache->v;
+    dp.k_scale = cache->k_scale;
+    dp.v_scale = cache->v_scale;
+    dp.tables = block_tables;
+    dp.ctx = context_lens;
+    dp.o = out;
+    dp.lse = out_lse;
+    dp.batch = num_seqs;
+    dp.num_q_heads = num_q_heads;
+    dp.num_kv_heads = cache->num_kv_heads;
+    dp.max_blocks = max_blocks_per_seq;
+    dp.num_blocks = cache->num_blocks;
+    dp.direct = 1;
+    dp.scale_log2 = p.scale_log2;
+    dp.cu_q = cu_q_lens;
+    dp.max_q_len = max_q_len;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (cache->kv_dtype) {
+      case PKV_BF16: e = pkv::launch_decode_rows_bf16(dp, cache->head_dim, group, st); break;
+      case PKV_I8: e = pkv::launch_decode_rows_i8(dp, cache->head_dim, group, st); break;
+      default: e = pkv::launch_decode_rows_fp8(dp, cache->head_dim, group, st); break;
+    }
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+  }
   const hipError_t e = pkv::launch_chunked(p, cache->kv_dtype, cache->head_dim, num_q_heads / cache->num_kv_heads,
                                            static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return fail(PKV_ERR_UNSUPPORTED, "%s: this configuration is not built", fn);
@@ -549,6 +652,11 @@ pkv_status pkv_paged_attention_decode_noalloc(const void* q, int32_t q_dtype, in
     return fail(PKV_ERR_WORKSPACE, "%s: needs %zu bytes of scratch, the library holds %zu per device "
                 "(fewer splits or a smaller batch per call, or pkv_paged_attention_decode with a workspace)",
                 fn, need, kScratchBytes);
+  if (pkv_status st = debug_validate(fn, decode_request(batch, cache, block_tables, max_blocks_per_seq, context_lens,
+                                                        num_splits, max_num_splits),
+                                     stream);
+      st != PKV_OK)
+    return st;
   void* ws = nullptr;
   if (need > 0) {
     if (pkv_status st = scratch_address(fn, &ws); st != PKV_OK) return st;

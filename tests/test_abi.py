@@ -198,3 +198,12 @@ def test_stream_read_rejects_bad_arguments():
     assert L.pkv_stream_read_workgroups(16) == 1
     assert L.pkv_stream_read_workgroups(34 << 20) == 2176      # 2,228,224 chunks / 1,024 per pass
     assert L.pkv_stream_read_workgroups(1 << 30) == 4096
+
+
+def test_debug_mode_keeps_host_checks_first(monkeypatch):
+    """With PKV_DEBUG=1 a call that fails a host check still returns before
+    the device validation pass (nothing is launched here)."""
+    monkeypatch.setenv("PKV_DEBUG", "1")
+    assert dec(cache(), q=None) == -1
+    assert "PKV_DEBUG" not in pkv.lib().pkv_last_error().decode()
+    assert dec(cache(), ws=None) == -3
