@@ -117,16 +117,20 @@ WORKLOADS = {
     "mixed_fp8_decode": (lambda W, seed, mts, batch, r: W.mixed_int8(seed=seed + 1000 * r, kv_dtype="fp8",
                                                                       max_tokens_per_split=mts or MIXED_SPLIT),
                          1, MIXED_SPLIT, {"workload": "mixed_fp8_step_decode_rows", "context_lens": "uniform[256,4096]"}),
+    # the same decode rows over a bf16 cache: the int8 rows' traffic compared at the same tokens
+    "mixed_bf16_decode": (lambda W, seed, mts, batch, r: W.mixed_int8(seed=seed + 1000 * r, kv_dtype="bf16",
+                                                                       max_tokens_per_split=mts or MIXED_SPLIT),
+                          1, MIXED_SPLIT, {"workload": "mixed_bf16_step_decode_rows", "context_lens": "uniform[256,4096]"}),
 }
 DEFAULT_SEEDS = {"qwen3_decode": 1902, "ragged_decode": 1903, "long_decode": 1904, "mixed_int8_decode": 1905,
-                 "mixed_fp8_decode": 1905}
+                 "mixed_fp8_decode": 1905, "mixed_bf16_decode": 1905}
 # Decode mode measured fastest on MI355X per shape: one workgroup per
 # (split, kv head) for the Qwen3 step (one split per sequence), the uniform
 # long contexts (64 splits of 512 tokens, as the workload states) and the
 # mixed step's decode rows (1024-token splits); the log-uniform ragged batch
 # gains from the balanced deal of tiles.
 DEFAULT_MODES = {"qwen3_decode": "splits", "ragged_decode": "balanced", "long_decode": "splits",
-                 "mixed_int8_decode": "splits", "mixed_fp8_decode": "splits"}
+                 "mixed_int8_decode": "splits", "mixed_fp8_decode": "splits", "mixed_bf16_decode": "splits"}
 # the other decode configurations reported beside the headline one (each in
 # its default mode and split plan)
 OTHER_CONFIGS = ("ragged_decode", "long_decode", "mixed_int8_decode")

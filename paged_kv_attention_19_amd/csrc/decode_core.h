@@ -29,7 +29,10 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
-template <int KV, int QT, int D, int G>
+// kCausal: the G rows are query rows at different positions of one
+// sequence (several new rows per sequence, each with its GQA heads), and row g
+// sees only tokens t <= lim[g]; every tile then carries its first token index.
+template <int KV, int QT, int D, int G, bool kCausal = false>
 struct WaveDecoder {
   using Geo = KvGeom<KV>;
   static constexpr int EPL = Geo::kEpl;                 // elements per 16-byte chunk
@@ -56,6 +59,7 @@ struct WaveDecoder {
     float ks[IPB];
     float vs[IPB];
     int rows;   // token rows of the tile that are read (0 .. 16)
+    int tok0;   // kCausal: sequence index of the tile's first token
   };
 
   int lane, tslot, lc, lane_off;
@@ -67,6 +71,7 @@ struct WaveDecoder {
   float qbias[G], qinv[G];
   bool q_ready;
   float m[G], l[G], acc[G][NE];
+  int lim[G];   // kCausal: row g sees tokens t <= lim[g] (set by the caller)
 
   __device__ __forceinline__ void init_lane() {
     lane = threadIdx.x & 63;
@@ -101,6 +106,35 @@ struct WaveDecoder {
           const float* qp = static_cast<const float*>(q) + base;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) qf[g][j * EPL + e] = qp[e];
+        }
+      }
+    }
+  }
+
+  // kCausal: the G query rows at element offsets off[g] of q (bf16); rows
+  // with live[g] false are zeros.
+  __device__ __forceinline__ void load_q_rows(const void* q, const int64_t (&off)[G], const bool (&live)[G]) {
+    static_assert(QT == PKV_BF16, "multi-row decode takes bf16 q");
+    q_ready = false;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int64_t base = off[g] + (j * LPT + lc) * EPL;
+        if constexpr (kDot2 || kDot2I8) {
+#pragma unroll
+          for (int u = 0; u < EPL / 8; ++u) {
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (live[g]) x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + base + 8 * u);
+            q2[g][j * (EPL / 2) + 4 * u + 0] = x.x;
+            q2[g][j * (EPL / 2) + 4 * u + 1] = x.y;
+            q2[g][j * (EPL / 2) + 4 * u + 2] = x.z;
+            q2[g][j * (EPL / 2) + 4 * u + 3] = x.w;
+          }
+        } else {
+          const uint16_t* qp = static_cast<const uint16_t*>(q) + base;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) qf[g][j * EPL + e] = live[g] ? __uint_as_float(static_cast<uint32_t>(qp[e]) << 16) : 0.f;
         }
       }
     }
@@ -209,6 +243,7 @@ struct WaveDecoder {
         for (int j = 0; j < CPL; ++j) unpack16<KV>(t.k[i][j], kf + j * EPL);
       }
       const bool valid = i * TPI + tslot < t.rows;
+      const int tok = kCausal ? t.tok0 + i * TPI + tslot : 0;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float d = 0.f;
@@ -234,7 +269,8 @@ struct WaveDecoder {
         d = group_sum<LPT>(d);
         if constexpr (kScaled) d *= t.ks[i] * scale_log2;
         else d *= scale_log2;
-        sc[i][g] = valid ? d : neg_inf();
+        if constexpr (kCausal) sc[i][g] = (valid && tok <= lim[g]) ? d : neg_inf();
+        else sc[i][g] = valid ? d : neg_inf();
       }
     }
     // online softmax: move the reference max only when a block exceeds it by
@@ -317,11 +353,13 @@ struct WaveDecoder {
       const int ids = (lane < cn && !lane_bad) ? v : 0;
       auto issue = [&](int it, Tile& t) {
         int rows = 0, id = 0;
+        const int first = tok0 + (c0 + it) * stride * kBlock;
         if (it < cn) {
-          rows = min(kBlock, t1 - (tok0 + (c0 + it) * stride * kBlock));
+          rows = min(kBlock, t1 - first);
           id = readlane(ids, it);
         }
         load_tile(p, id, kh, rows, t);
+        if constexpr (kCausal) t.tok0 = first;
       };
 #pragma unroll
       for (int k = 0; k < PD; ++k) issue(k, ring[k]);

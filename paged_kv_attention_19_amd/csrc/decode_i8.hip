@@ -8,4 +8,8 @@ hipError_t launch_decode_partial_i8(const DecodeParams& p, int q_dtype, int head
   return launch_partial_kv<PKV_I8>(p, q_dtype, head_dim, group, waves, st);
 }
 
+hipError_t launch_decode_rows_i8(const DecodeParams& p, int head_dim, int group, hipStream_t st) {
+  return launch_rows_kv<PKV_I8>(p, head_dim, group, st);
+}
+
 }  // namespace pkv

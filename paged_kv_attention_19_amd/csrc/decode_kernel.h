@@ -270,6 +270,188 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
   }
 }
 
+// Several new rows per sequence: the L_b rows of sequence b (chunk rows at
+// positions n_b - L_b + r; speculative verification, or any chunk of a few
+// rows) with the GQ query heads of kv head kh, R = L * GQ rows in all (padded
+// to a power of two), share every K/V tile the wavefronts stream, as the GQA
+// heads of one decode row do. Row r sees tokens t <= n_b - L_b + r (course
+// README "Build an LLM Inference Engine From Scratch", curriculum S11 chunked
+// prefill: a chunk's rows attend the cached prefix and the chunk's own earlier
+// rows). One workgroup of NW wavefronts per (sequence, kv head) streams the
+// whole sequence, blocks dealt round-robin, and merges through LDS.
+template <int KV, int D, int GQ, int R, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_rows_kernel(DecodeParams p) {
+  using WD = WaveDecoder<KV, PKV_BF16, D, R, true>;
+  constexpr int LPT = WD::LPT, TPI = WD::TPI, CPL = WD::CPL, EPL = WD::EPL;
+  static_assert(R % GQ == 0, "whole rows");
+  constexpr bool kLdsMerge = NW * TPI * R * D * 4 <= 65536;
+  constexpr int kSlots = kLdsMerge ? TPI : 1;
+  __shared__ float s_part[NW][kSlots][R][D];
+  __shared__ float s_lp[NW][kSlots][R];
+  __shared__ float s_m[NW][R];
+  __shared__ int s_bad[NW];
+
+  const int nwg = gridDim.x;
+  const int item = (blockIdx.x % kXcds) * (nwg / kXcds) + blockIdx.x / kXcds;
+  if (item >= p.batch * p.num_kv_heads) return;   // grid padding
+  const int kh = item % p.num_kv_heads;
+  const int b = item / p.num_kv_heads;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Hq = p.num_q_heads;
+
+  WD wd;
+  wd.init_lane();
+  const int lane = wd.lane;
+  int early_ids = 0;
+  {
+    const int j = w + NW * lane;
+    if (j < p.max_blocks) early_ids = p.tables[static_cast<size_t>(b) * p.max_blocks + j];
+  }
+  const int n = p.ctx[b];
+  const int q0 = p.cu_q[b];
+  const int L = p.cu_q[b + 1] - q0;
+  if (L == 0) return;
+  const bool bad_seq = L < 0 || L > p.max_q_len || L * GQ > R || n < L ||
+                       static_cast<int64_t>(n) > static_cast<int64_t>(p.max_blocks) * kBlock;
+  if (bad_seq) {
+    // the chunk's rows of this kv head's query heads become NaN
+    for (int64_t idx = threadIdx.x; idx < static_cast<int64_t>(max(L, 0)) * GQ * D; idx += NW * kWave) {
+      const int64_t r = idx / (GQ * D);
+      const int gh = static_cast<int>((idx / D) % GQ);
+      const size_t row = static_cast<size_t>(q0 + r) * Hq + kh * GQ + gh;
+      p.o[row * D + idx % D] = qnan();
+      if (idx % D == 0 && p.lse != nullptr) p.lse[row] = qnan();
+    }
+    return;
+  }
+
+  int64_t off[R];
+  bool live[R];
+#pragma unroll
+  for (int g = 0; g < R; ++g) {
+    const int r = g / GQ;
+    live[g] = r < L;
+    off[g] = (static_cast<int64_t>(q0 + (live[g] ? r : 0)) * Hq + kh * GQ + g % GQ) * D;
+    wd.lim[g] = n - L + r;
+  }
+  const int nblk = (n + kBlock - 1) / kBlock;
+  const int nb_w = nblk > w ? (nblk - w + NW - 1) / NW : 0;
+  wd.reset();
+  bool bad = false;
+  wd.template stream_blocks<1>(p, kh, p.tables + static_cast<size_t>(b) * p.max_blocks + w, NW, w * kBlock, nb_w, n,
+                               true, early_ids, bad, [&] { wd.load_q_rows(p.q, off, live); });
+
+  // merge the wave's token slots, then the wavefronts, as the split decode does
+  float M[R];
+  wd.slots_to_common_max(M);
+  const int tslot = wd.tslot, lc = wd.lc;
+  if constexpr (kLdsMerge) {
+#pragma unroll
+    for (int g = 0; g < R; ++g) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s_part[w][tslot][g][wd.dim_of(j, e)] = wd.acc[g][j * EPL + e];
+      }
+      if (lc == 0) s_lp[w][tslot][g] = wd.l[g];
+    }
+  } else {
+    wd.sum_slots();
+    if (lane < LPT) {
+#pragma unroll
+      for (int g = 0; g < R; ++g) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) s_part[w][0][g][wd.dim_of(j, e)] = wd.acc[g][j * EPL + e];
+        }
+        if (lc == 0) s_lp[w][0][g] = wd.l[g];
+      }
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < R; ++g) s_m[w][g] = M[g];
+    s_bad[w] = bad ? 1 : 0;
+  }
+  __syncthreads();
+
+  bool any_bad = false;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) any_bad = any_bad || (s_bad[ww] != 0);
+
+  for (int idx = threadIdx.x; idx < R * D; idx += NW * kWave) {
+    const int g = idx / D;
+    const int d = idx % D;
+    const int r = g / GQ;
+    if (r >= L) continue;
+    float Mx = neg_inf();
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) Mx = fmaxf(Mx, s_m[ww][g]);
+    float Ls = 0.f, O = 0.f;
+    if (Mx != neg_inf()) {
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float mw = s_m[ww][g];
+        const float wt = (mw == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
+        float ls = 0.f, os = 0.f;
+#pragma unroll
+        for (int t = 0; t < kSlots; ++t) {
+          ls += s_lp[ww][t][g];
+          os += s_part[ww][t][g][d];
+        }
+        Ls += ls * wt;
+        O += os * wt;
+      }
+    }
+    float o, lse;
+    if (any_bad) {
+      o = qnan();
+      lse = qnan();
+    } else {
+      o = O * norm_inv(Ls);
+      lse = norm_lse2(Mx, Ls);
+    }
+    const size_t row = static_cast<size_t>(q0 + r) * Hq + kh * GQ + g % GQ;
+    p.o[row * D + d] = o;
+    if (d == 0 && p.lse != nullptr) p.lse[row] = lse;
+  }
+}
+
+template <int KV, int D, int GQ>
+hipError_t launch_rows_g(const DecodeParams& p, hipStream_t st) {
+  const int items = p.batch * p.num_kv_heads;
+  const int grid = (items + kXcds - 1) / kXcds * kXcds;
+  const int rows = p.max_q_len * GQ;   // query rows sharing each K/V tile
+  if constexpr (GQ <= 2) {
+    if (rows <= 2) {
+      hipLaunchKernelGGL((decode_rows_kernel<KV, D, GQ, 2, 4>), dim3(grid), dim3(4 * kWave), 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (GQ <= 4) {
+    if (rows <= 4) {
+      hipLaunchKernelGGL((decode_rows_kernel<KV, D, GQ, 4, 4>), dim3(grid), dim3(4 * kWave), 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  if (rows > 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_rows_kernel<KV, D, GQ, 8, 4>), dim3(grid), dim3(4 * kWave), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int KV>
+hipError_t launch_rows_kv(const DecodeParams& p, int head_dim, int group, hipStream_t st) {
+  if (head_dim != 128) return hipErrorInvalidValue;
+  switch (group) {
+    case 1: return launch_rows_g<KV, 128, 1>(p, st);
+    case 2: return launch_rows_g<KV, 128, 2>(p, st);
+    case 4: return launch_rows_g<KV, 128, 4>(p, st);
+    case 8: return launch_rows_g<KV, 128, 8>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 __device__ __forceinline__ int wave_sum_i32(int x) {
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);

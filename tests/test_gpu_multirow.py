@@ -1,0 +1,162 @@
+"""GPU parity of the chunked entry point's path for chunks of a few rows
+(speculative verification: k draft rows per sequence). When max_q_len times
+the GQA group is at most 4, the rows are computed by the decode kernels,
+every chunk row of a kv head's query heads on each K/V tile, with row r of an
+L-row chunk seeing tokens t <= n - L + r. Same tolerance as the other decode
+tests; indexing checked bit for bit with a one-hot probe."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads as W
+from tests import gpu_side as G
+from tests import oracle_side as O
+
+pytestmark = pytest.mark.gpu
+
+
+def check(got, ref, what):
+    st = O.compare(got, ref)
+    print(f"{what}: max_abs {st['max_abs']:.3g} max_rel {st['max_rel']:.3g} over {st['n']}")
+    assert st["ok"], f"{what}: {st}"
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
+@pytest.mark.parametrize("Hq,Hkv,ql", [
+    (16, 8, [2, 1, 2, 2, 1, 2]),       # group 2: up to 2 rows (4 rows per kv head)
+    (8, 8, [4, 3, 1, 4, 4, 2]),        # group 1: up to 4 rows
+    (16, 4, [1, 1, 1, 1, 1, 1]),       # group 4: one row per sequence through the chunked call
+    (16, 8, [1, 1, 1, 1, 1, 1]),       # group 2: one row (2 rows per kv head)
+])
+def test_few_row_chunks_match_oracle(gpu, kv, Hq, Hkv, ql):
+    ctx = [300, 77, 1025, 8, 129, 2000]
+    step = W.make_step(f"rows_{kv}_{Hq}_{Hkv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,
+                       kv_dtype=kv, src_dtype="bf16", seed=600 + Hkv + max(ql))
+    assert max(ql) * (Hq // Hkv) <= 4
+    cache = G.build_cache(step, gpu)
+    # every sequence's rows as one chunk each (one-row chunks included)
+    q, cu, tables, ctx = step.q, step.cu_q_lens, step.block_tables, step.context_lens
+    G.announce(f"few-row chunks {step.name} max_q_len={max(ql)}")
+    out, lse = G.pkv.paged_attention_chunked(G.tensor(q, "bf16", gpu), G.ints(cu, gpu), max(ql), cache,
+                                             G.ints(tables, gpu), G.ints(ctx, gpu), float(step.scale),
+                                             return_lse=True)
+    import torch
+    torch.cuda.synchronize()
+    ro, rl = O.oracle.paged_chunked(O.oracle.decode_rows(q, "bf16"), cu, O.pool(step), tables, ctx, step.scale)
+    check(out.cpu().numpy(), ro, "out")
+    check(lse.cpu().numpy(), rl, "lse")
+
+
+def test_spec_verify_shape_matches_oracle(gpu):
+    """The benchmark's verification shape: 32 sequences of 128..384 tokens,
+    4 new rows each, Qwen3 heads, bf16 (8 rows per kv head: the MFMA kernel)."""
+    rng = np.random.default_rng(np.random.SeedSequence([1906, 7]))
+    ctx = rng.integers(128, 384, size=32, endpoint=True)
+    step = W.make_step("spec_verify", ctx, np.full(32, 4), num_q_heads=16, num_kv_heads=8, head_dim=128,
+                       num_blocks=4096, seed=1906)
+    cache = G.build_cache(step, gpu)
+    out, lse = G.run_chunked(step, cache, gpu)
+    ro, rl = O.chunked(step, O.pool(step))
+    check(out, ro, "out")
+    check(lse, rl, "lse")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_few_row_one_hot_rows_before_and_after_the_hot_key(gpu, kv):
+    """2 rows per sequence at positions n-2, n-1 (4 rows per kv head: the
+    decode kernels); key 0 is warm, key n-1 is hot, every other key zero: row
+    n-2 returns V_0 and row n-1 returns V_{n-1}, bit for bit."""
+    import torch
+    Hq, Hkv, D = 16, 8, 128
+    ctx = [300, 45, 17]
+    ql = [2, 2, 2]
+    step = W.make_step(f"rows1hot_{kv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, kv_dtype=kv,
+                       src_dtype="bf16", seed=610)
+    rng = np.random.default_rng(611)
+    slots, Ks, Vs = [], [], []
+    for i, n in enumerate(ctx):
+        k = np.zeros((n, Hkv, D), np.float32)
+        k[0, :, :8] = 32.0
+        k[n - 1, :, :8] = 128.0
+        Ks.append(k)
+        Vs.append(rng.standard_normal((n, Hkv, D)).astype(np.float32))
+        t = np.arange(n)
+        slots.append(step.block_tables[i, t // 16].astype(np.int64) * 16 + t % 16)
+    Kb, Vb = W.f32_to_bf16_bits(np.concatenate(Ks)), W.f32_to_bf16_bits(np.concatenate(Vs))
+    sl = np.concatenate(slots)
+    cache = G.pkv.KVCache.allocate(step.num_blocks, Hkv, D, G.CODE[kv], gpu)
+    G.pkv.reshape_and_cache(G.tensor(Kb, "bf16", gpu), G.tensor(Vb, "bf16", gpu), G.ints(sl, gpu, torch.int64), cache)
+    pool = O.oracle.OraclePool(step.num_blocks, Hkv, 16, D, kv)
+    O.oracle.reshape_and_cache(pool, Kb, Vb, "bf16", sl)
+    qv = np.zeros((sum(ql), Hq, D), np.float32)
+    qv[:, :, :8] = 1.0
+    cu = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    G.announce(f"few-row one-hot kv={kv}")
+    out = G.pkv.paged_attention_chunked(G.tensor(W.f32_to_bf16_bits(qv), "bf16", gpu), G.ints(cu, gpu), 2, cache,
+                                        G.ints(step.block_tables, gpu), G.ints(np.array(ctx), gpu), 1.0)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for i, n in enumerate(ctx):
+        _, V = O.oracle.gather_kv(pool, step.block_tables[i], n)
+        for r in range(2):
+            src = n - 1 if n - 2 + r >= n - 1 else 0
+            for h in range(Hq):
+                assert np.array_equal(out[cu[i] + r, h], V[src, h // 2].astype(np.float32)), (kv, i, r, h)
+
+
+def test_few_row_path_agrees_with_the_mfma_path(gpu):
+    """The same 2-row chunks through the few-row path (16 q / 8 kv heads,
+    4 rows per kv head) and, with a larger max_q_len, through the MFMA
+    kernel: both within tolerance of the oracle and of each other."""
+    import torch
+    step = W.make_step("rows_vs_mfma", [300, 77, 1025], [2, 2, 2], num_q_heads=16, num_kv_heads=8, head_dim=128,
+                       seed=612)
+    cache = G.build_cache(step, gpu)
+    q, cu, tables, ctx = step.chunk_batch()
+    args = (G.tensor(q, "bf16", gpu), G.ints(cu, gpu))
+    G.announce("few-row vs MFMA path")
+    a = G.pkv.paged_attention_chunked(*args, 2, cache, G.ints(tables, gpu), G.ints(ctx, gpu), float(step.scale))
+    b = G.pkv.paged_attention_chunked(*args, 64, cache, G.ints(tables, gpu), G.ints(ctx, gpu), float(step.scale))
+    torch.cuda.synchronize()
+    a, b = a.cpu().numpy(), b.cpu().numpy()
+    ro, _ = O.chunked(step, O.pool(step))
+    check(a, ro, "few-row")
+    check(b, ro, "mfma")
+    check(a, b.astype(np.float64), "few-row vs mfma")
+
+
+def test_few_row_bad_metadata_and_empty_chunks(gpu):
+    """A chunk longer than its context or than max_q_len comes out NaN, an
+    out-of-pool block id poisons its sequence, a zero-row chunk writes
+    nothing, and the other sequences are unaffected (2-row chunks, 4 rows per
+    kv head: the decode kernels)."""
+    import torch
+    step = W.make_step("rows_bad", [100, 100, 100, 100], [2, 2, 2, 2], num_q_heads=16, num_kv_heads=8,
+                       head_dim=128, seed=613)
+    cache = G.build_cache(step, gpu)
+    ro, _ = O.chunked(step, O.pool(step))
+    q, cu, tables, ctx = step.chunk_batch()
+    ctx = ctx.copy()
+    tables = tables.copy()
+    ctx[0] = 1                         # shorter than its 2-row chunk
+    tables[1, 3] = step.num_blocks + 4
+    cu2 = cu.copy()
+    cu2[3] = cu2[2]                    # sequence 2 has an empty chunk; sequence 3 takes 4 rows
+    G.announce("few-row bad metadata")
+    out = torch.full((len(q), 16, 128), 7.0, dtype=torch.float32, device=gpu)
+    G.pkv.paged_attention_chunked(G.tensor(q, "bf16", gpu), G.ints(cu2, gpu), 2, cache, G.ints(tables, gpu),
+                                  G.ints(ctx, gpu), float(step.scale), out=out)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.isnan(out[0:2]).all()          # sequence 0: chunk longer than its context
+    assert np.isnan(out[2:4]).all()          # sequence 1: block id outside the pool
+    assert np.isnan(out[4:8]).all()          # sequence 3: 4 rows > max_q_len = 2
+    G.announce("few-row clean rerun")
+    out2 = G.pkv.paged_attention_chunked(G.tensor(q, "bf16", gpu), G.ints(cu, gpu), 2, cache,
+                                         G.ints(step.chunk_batch()[2], gpu), G.ints(step.chunk_batch()[3], gpu),
+                                         float(step.scale))
+    torch.cuda.synchronize()
+    check(out2.cpu().numpy(), ro, "clean rerun")
+

@@ -269,7 +269,7 @@ def mixed_int8(num_prefill: int = 4, chunk: int = 512, prefix: int = 1536, num_d
                lo: int = 256, hi: int = 4096, max_tokens_per_split: int = 512,
                seed: int = 1905, kv_dtype: str = I8) -> Step:
     """Mixed chunked-prefill + decode step over an int8 (or, with ``kv_dtype=
-    "fp8"``, an fp8) KV cache: ``num_prefill``
+    "fp8"``, an fp8; with ``"bf16"``, a bf16 one of the same shape) KV cache: ``num_prefill``
     sequences with a ``chunk``-row causal chunk after a ``prefix``-token cached
     prefix, plus ``num_decode`` decode rows with n uniform in [256, 4096].
     16q/8kv/128, q and the new K/V rows bf16 (quantized by the cache write),
@@ -278,7 +278,8 @@ def mixed_int8(num_prefill: int = 4, chunk: int = 512, prefix: int = 1536, num_d
     dec = rng.integers(lo, hi, size=num_decode, endpoint=True)
     ctx = np.concatenate([np.full(num_prefill, prefix + chunk), dec]).astype(np.int64)
     ql = np.concatenate([np.full(num_prefill, chunk), np.ones(num_decode)]).astype(np.int64)
-    assert kv_dtype in (I8, FP8)
-    return make_step("mixed_int8" if kv_dtype == I8 else "mixed_fp8", ctx, ql, num_q_heads=16, num_kv_heads=8,
+    assert kv_dtype in (I8, FP8, BF16)
+    name = {I8: "mixed_int8", FP8: "mixed_fp8", BF16: "mixed_bf16"}[kv_dtype]
+    return make_step(name, ctx, ql, num_q_heads=16, num_kv_heads=8,
                      head_dim=128, q_dtype=BF16, kv_dtype=kv_dtype, src_dtype=BF16,
                      num_splits=splits_for(ctx, max_tokens_per_split), seed=seed)
