@@ -144,6 +144,11 @@ int decode_waves(int /*max_blocks_per_seq*/, int /*max_num_splits*/) {
 // 2: 9.9-10.1 against 18.0-18.8 us; 4: 13.0-13.2 against 18.1-18.8 us; 8:
 // 23.8-25.0 against 18.3-19.9 us.
 constexpr int kRowsDecodeMax = 4;
+// Up to 16 rows per kv head: a decode-shaped kernel on 16x16 MFMAs (one
+// workgroup per (sequence, kv head), the rows as the MFMA's N side). Same
+// workload: 15.2 us at 8 rows per kv head (L 4, G 2) and 16.6 us at 16 (L 8,
+// G 2 or L 16, G 1), against 18.9-20.2 us on the 128-row MFMA kernel.
+constexpr int kRowsMfmaMax = 16;
 
 constexpr int kBalancedMaxWorkgroups = 512;
 size_t balanced_part_bytes(int heads_per_slot, int head_dim) {
@@ -592,7 +597,7 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
   dr.max_q_len = max_q_len;
   if (pkv_status st = debug_validate(fn, dr, stream); st != PKV_OK) return st;
   const int group = num_q_heads / cache->num_kv_heads;
-  if (static_cast<int64_t>(max_q_len) * group <= kRowsDecodeMax) {
+  if (static_cast<int64_t>(max_q_len) * group <= kRowsMfmaMax) {
     // chunks of a few rows (speculative verification): the decode kernels,
     // with every chunk row of a kv head's query heads on each K/V tile
     pkv::DecodeParams dp{};
@@ -616,10 +621,14 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
     dp.max_q_len = max_q_len;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    switch (cache->kv_dtype) {
-      case PKV_BF16: e = pkv::launch_decode_rows_bf16(dp, cache->head_dim, group, st); break;
-      case PKV_I8: e = pkv::launch_decode_rows_i8(dp, cache->head_dim, group, st); break;
-      default: e = pkv::launch_decode_rows_fp8(dp, cache->head_dim, group, st); break;
+    if (static_cast<int64_t>(max_q_len) * group > kRowsDecodeMax) {
+      e = pkv::launch_rows_mfma(dp, cache->kv_dtype, cache->head_dim, group, st);
+    } else {
+      switch (cache->kv_dtype) {
+        case PKV_BF16: e = pkv::launch_decode_rows_bf16(dp, cache->head_dim, group, st); break;
+        case PKV_I8: e = pkv::launch_decode_rows_i8(dp, cache->head_dim, group, st); break;
+        default: e = pkv::launch_decode_rows_fp8(dp, cache->head_dim, group, st); break;
+      }
     }
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();

@@ -153,6 +153,8 @@ hipError_t launch_decode_partial_fp8(const DecodeParams& p, int q_dtype, int hea
 hipError_t launch_decode_rows_bf16(const DecodeParams& p, int head_dim, int group, hipStream_t stream);
 hipError_t launch_decode_rows_i8(const DecodeParams& p, int head_dim, int group, hipStream_t stream);
 hipError_t launch_decode_rows_fp8(const DecodeParams& p, int head_dim, int group, hipStream_t stream);
+// The same rows on MFMA (rows_mfma.hip): max_q_len * group <= 16, bf16 q, head_dim 128.
+hipError_t launch_rows_mfma(const DecodeParams& p, int kv_dtype, int head_dim, int group, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_chunked(const ChunkedParams& p, int kv_dtype, int head_dim, int group,
                           hipStream_t stream);
