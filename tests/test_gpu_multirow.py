@@ -1,6 +1,7 @@
-"""GPU parity of the chunked entry point's path for chunks of a few rows
+"""GPU parity of the chunked entry point's paths for chunks of a few rows
 (speculative verification: k draft rows per sequence). When max_q_len times
-the GQA group is at most 4, the rows are computed by the decode kernels,
+the GQA group is at most 4, the rows are computed by the decode kernels (up
+to 16: by a decode-shaped kernel on 16x16 MFMAs),
 every chunk row of a kv head's query heads on each K/V tile, with row r of an
 L-row chunk seeing tokens t <= n - L + r. Same tolerance as the other decode
 tests; indexing checked bit for bit with a one-hot probe."""
