@@ -578,8 +578,9 @@ def measure_spec_verify(dev, min_seconds):
     sec, nwin, _ = time_windows(call, reps, steps, 256, 64, min_seconds)
     per = sec / steps
     kv = sum(r["kv"] for r in reps) / len(reps)
-    return {"config": "spec_verify_b32_q4", "entry_point": "pkv_paged_attention_chunked", "kernel": "chunked_kernel",
-            "rows_per_seq": 4, "context_lens": "uniform[128,384]", "kv_bytes_per_step": int(kv),
+    return {"config": "spec_verify_b32_q4", "entry_point": "pkv_paged_attention_chunked",
+            "kernel": "rows_mfma_kernel (8 rows per kv head)", "rows_per_seq": 4, "context_lens": "uniform[128,384]",
+            "kv_bytes_per_step": int(kv),
             "us_per_step": round(per * 1e6, 2), "GB/s": round(kv / per / 1e9, 1),
             "hbm_peak_frac": round(kv / per / 1e9 / HBM_PEAK_GBS, 4), "seq_steps_per_s": round(32 / per, 1),
             "windows": nwin}
