@@ -2,8 +2,9 @@
 size, cache and q dtype the library builds, random context lengths (block
 multiples and ragged tails), random split counts (past the block count too:
 empty splits), split and balanced decode modes, and random chunk / prefix
-lengths for chunked prefill. The cases are drawn once, from a fixed seed, so
-every run tests the same ones."""
+lengths for chunked prefill, and chunks of a few rows per sequence (the
+decode-shaped paths of the chunked call). The cases are drawn once, from a
+fixed seed, so every run tests the same ones."""
 
 from __future__ import annotations
 
@@ -53,8 +54,28 @@ def _chunked_cases(n_cases: int = 16, seed: int = 20261203):
     return cases
 
 
+def _few_row_cases(n_cases: int = 12, seed: int = 20261204):
+    """Chunks of 1 to 16 / G rows per sequence, one-row chunks among them, over
+    random prefixes: up to 4 rows per kv head take the decode kernels, 5 to 16
+    the 16x16 MFMA kernel."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n_cases):
+        g = int(rng.choice([1, 2, 4, 8]))
+        hkv = int(rng.choice([1, 2, 4]))
+        kv = str(rng.choice(["bf16", "i8", "fp8"]))
+        S = int(rng.integers(1, 25))
+        lmax = int(rng.integers(1, 16 // g + 1))
+        L = rng.integers(1, lmax + 1, size=S)
+        prefix = rng.integers(0, 900, size=S)
+        cases.append(dict(id=f"r{i}_g{g}_h{hkv}_{kv}_S{S}_L{int(L.max())}", g=g, hkv=hkv, kv=kv,
+                          ctx=[int(a + b) for a, b in zip(prefix, L)], ql=[int(x) for x in L], seed=5000 + i))
+    return cases
+
+
 DECODE = _decode_cases()
 CHUNKED = _chunked_cases()
+FEW_ROWS = _few_row_cases()
 
 
 def _check(out, ref, what, case):
@@ -94,3 +115,22 @@ def test_random_chunked(gpu, case):
     ro, rl = O.chunked(step, O.pool(step))
     _check(out, ro, "out", case)
     _check(lse, rl, "lse", case)
+
+
+@pytest.mark.parametrize("case", FEW_ROWS, ids=[c["id"] for c in FEW_ROWS])
+def test_random_few_row_chunks(gpu, case):
+    import torch
+    step = W.make_step(case["id"], case["ctx"], case["ql"], num_q_heads=case["g"] * case["hkv"],
+                       num_kv_heads=case["hkv"], head_dim=128, kv_dtype=case["kv"], src_dtype="bf16",
+                       seed=case["seed"])
+    cache = G.build_cache(step, gpu)
+    # every sequence's rows as one chunk (one-row chunks included)
+    q, cu, tables, ctx = step.q, step.cu_q_lens, step.block_tables, step.context_lens
+    G.announce(f"few-row chunks {case['id']}")
+    out, lse = G.pkv.paged_attention_chunked(G.tensor(q, "bf16", gpu), G.ints(cu, gpu), int(max(case["ql"])), cache,
+                                             G.ints(tables, gpu), G.ints(ctx, gpu), float(step.scale),
+                                             return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = O.oracle.paged_chunked(O.oracle.decode_rows(q, "bf16"), cu, O.pool(step), tables, ctx, step.scale)
+    _check(out.cpu().numpy(), ro, "out", case)
+    _check(lse.cpu().numpy(), rl, "lse", case)
