@@ -42,11 +42,14 @@ if ROOT not in sys.path:
 METRIC = "paged-attn decode KV GB/s (% HBM peak) + seq-steps/s; chunked-prefill MFMA util"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16, published
+# the files a kernel's code is built from (its per-source compiler flags
+# included): profile figures recorded for other contents are not used
 DECODE_FILES = ("paged_kv_attention_19_amd/csrc/decode_kernel.h", "paged_kv_attention_19_amd/csrc/decode_core.h",
                 "paged_kv_attention_19_amd/csrc/decode_bf16.hip", "paged_kv_attention_19_amd/csrc/pkv_device.h",
-                "paged_kv_attention_19_amd/csrc/quant_row.h", "paged_kv_attention_19_amd/csrc/api.hip")
+                "paged_kv_attention_19_amd/csrc/quant_row.h", "paged_kv_attention_19_amd/csrc/api.hip",
+                "paged_kv_attention_19_amd/build.py")
 CHUNKED_FILES = ("paged_kv_attention_19_amd/csrc/chunked.hip", "paged_kv_attention_19_amd/csrc/pkv_device.h",
-                 "paged_kv_attention_19_amd/csrc/api.hip")
+                 "paged_kv_attention_19_amd/csrc/api.hip", "paged_kv_attention_19_amd/build.py")
 DECODE_PROFILE = os.path.join(ROOT, "profiles", "decode_partial_qwen3_traffic.json")
 CHUNKED_PROFILE = os.path.join(ROOT, "profiles", "chunked_kernel_mixed_int8_traffic.json")
 WINDOWS_MIN = 5
