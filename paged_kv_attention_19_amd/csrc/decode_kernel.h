@@ -815,11 +815,12 @@ hipError_t launch_balanced_t(const DecodeParams& p, int workgroups, hipStream_t 
 }
 
 // waves: wavefronts per workgroup. Each wavefront keeps one block of K/V in
-// flight while it reduces the previous one. Measured on MI355X (bf16, 16/8
-// heads, head_dim 128), per launch: the 32-sequence step of 128..384 tokens
-// takes 10.7 us with one block ahead, 10.9 / 11.5 / 12.0 us with 2 / 3 / 4
-// (each extra block costs 32 VGPRs, with no latency left to hide); 8 x 32k
-// tokens and the 4096-token int8 batch are within 1% of their best.
+// flight while it reduces the previous one. Measured on MI355X (16/8 heads,
+// head_dim 128), per step with one block ahead against two: the 32-sequence
+// bf16 step of 128..384 tokens 10.07 against 10.50 us, the mixed step's int8
+// rows 106.9 against 113.4 us, and 8 x 32k bf16 tokens 174.3 against 171.6
+// us. The host sees only the table width, which does not tell these apart,
+// so one block ahead is kept.
 template <int KV, int QT, int D, int G>
 hipError_t launch_partial_w(const DecodeParams& p, int waves, hipStream_t st) {
   if (waves < 0) return launch_balanced_t<KV, QT, D, G>(p, -waves, st);   // balanced: -workgroups
