@@ -10,55 +10,109 @@ namespace pkv {
 
 namespace {
 
-// One wavefront per (sequence, query head): merge that pair's split partials.
-template <int D>
+// NW = 4: one workgroup of 4 wavefronts per (sequence, query head).
+// Wavefront w merges splits w, w + 4, w + 8, ... against its own reference
+// max; the four states (M_w, L_w, acc_w) then merge through LDS, each
+// rescaled by exp(M_w - M). So the partials of a pair are read by four chains
+// of loads in parallel, not one. NW = 1: one wavefront per pair, four pairs
+// per workgroup, for pairs of a few splits, where the other three wavefronts
+// would have nothing to read.
+template <int D, int NW>
 __global__ __launch_bounds__(256) void lse_combine_kernel(CombineParams p) {
   constexpr int DPL = D / kWave;  // dims per lane
+  __shared__ float s_acc[NW][D];
+  __shared__ float s_m[NW], s_l[NW];
+  __shared__ int s_nan[NW];
   const int lane = threadIdx.x & 63;
-  const int pair = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = NW == 1 ? 0 : wid;   // this wavefront's first split
+  const int pair = NW == 1 ? blockIdx.x * 4 + wid : blockIdx.x;
   if (pair >= p.batch * p.num_q_heads) return;
   const int b = pair / p.num_q_heads;
   const int h = pair % p.num_q_heads;
   const int ns = p.nsplits[b];
-  float* out = p.out + static_cast<size_t>(pair) * D + lane * DPL;
   const bool bad = ns < 1 || ns > p.max_ns;
   const size_t row0 = static_cast<size_t>(b) * p.max_ns * p.num_q_heads + h;
 
-  float M = neg_inf();
+  // this wavefront's splits: their max lse (and whether any is NaN)
+  float Mw = neg_inf();
   bool nan = false;
   if (!bad) {
-    for (int s = lane; s < ns; s += kWave) {
+    for (int s = w + NW * lane; s < ns; s += NW * kWave) {
       const float x = p.lse_part[row0 + static_cast<size_t>(s) * p.num_q_heads];
       nan = nan || (x != x);
-      M = fmaxf(M, x);
+      Mw = fmaxf(Mw, x);
     }
   }
-  M = wave_max(M);
+  Mw = wave_max(Mw);
   nan = wave_any(nan);
-  float L = 0.f;
+  float Lw = 0.f;
   float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  if (!bad && !nan && M != neg_inf()) {
+  if (!bad && !nan && Mw != neg_inf()) {
 #pragma unroll 4
-    for (int s = 0; s < ns; ++s) {
+    for (int s = w; s < ns; s += NW) {
       const size_t row = row0 + static_cast<size_t>(s) * p.num_q_heads;
       const float x = p.lse_part[row];
-      const float wt = __builtin_amdgcn_exp2f((x - M) * kLog2e);  // -inf -> 0
-      L += wt;
+      const float wt = __builtin_amdgcn_exp2f((x - Mw) * kLog2e);  // -inf -> 0
+      Lw += wt;
       const float* o = p.o_part + row * D + lane * DPL;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wt, o[e], acc[e]);
     }
   }
+  float M, L;
+  bool any_nan;
+  float f[NW];
+  if constexpr (NW == 1) {
+    M = Mw;
+    L = Lw;
+    any_nan = nan;
+    f[0] = 1.f;
+  } else {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) s_acc[w][lane * DPL + e] = acc[e];
+    if (lane == 0) {
+      s_m[w] = Mw;
+      s_l[w] = Lw;
+      s_nan[w] = nan;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    M = s_m[0];
+    any_nan = s_nan[0] != 0;
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+      M = fmaxf(M, s_m[i]);
+      any_nan = any_nan || (s_nan[i] != 0);
+    }
+    L = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      f[i] = (s_m[i] == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f((s_m[i] - M) * kLog2e);
+      L += s_l[i] * f[i];
+    }
+  }
+  float* out = p.out + static_cast<size_t>(pair) * D + lane * DPL;
   float lse;
-  if (bad || nan) {
+  if (bad || any_nan) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) out[e] = qnan();
     lse = qnan();
   } else if (L > 0.f) {
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) out[e] = acc[e] / L;
+    for (int e = 0; e < DPL; ++e) {
+      float y;
+      if constexpr (NW == 1) {
+        y = acc[e];
+      } else {
+        y = 0.f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) y = fmaf(s_acc[i][lane * DPL + e], f[i], y);
+      }
+      out[e] = y / L;
+    }
     lse = M + logf(L);
   } else {
 #pragma unroll
@@ -70,15 +124,31 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(CombineParams p) {
 
 }  // namespace
 
-hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t st) {
+// Four wavefronts per pair from this many splits on (p.max_ns: the host's
+// bound on every sequence's split count). Measured on MI355X (traced, head_dim
+// 128, 16 query heads): 8 x 32k tokens in 64 splits, 6.7 us with one
+// wavefront per pair against 3.9 us with four (eight, or a deeper unroll, were
+// within noise of four); the mixed step's decode rows (at most 4 splits), 3.4
+// us either way.
+constexpr int kCombineWideSplits = 8;
+
+template <int D>
+hipError_t launch_combine_d(const CombineParams& p, hipStream_t st) {
   const int pairs = p.batch * p.num_q_heads;
-  const dim3 grid((pairs + 3) / 4);
-  switch (head_dim) {
-    case 64: hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(256), 0, st, p); break;
-    case 128: hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(256), 0, st, p); break;
-    default: return hipErrorInvalidValue;
+  if (p.max_ns >= kCombineWideSplits) {
+    hipLaunchKernelGGL((lse_combine_kernel<D, 4>), dim3(pairs), dim3(256), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((lse_combine_kernel<D, 1>), dim3((pairs + 3) / 4), dim3(256), 0, st, p);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t st) {
+  switch (head_dim) {
+    case 64: return launch_combine_d<64>(p, st);
+    case 128: return launch_combine_d<128>(p, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace pkv
