@@ -287,16 +287,21 @@ def test_output_is_bit_identical_under_block_placement(gpu):
     assert out1.tobytes() == out2.tobytes() and lse1.tobytes() == lse2.tobytes()
 
 
-def test_lse_combine_alone(gpu):
+@pytest.mark.parametrize("S,ns", [
+    (6, [1, 6, 3, 2, 6]),              # one wavefront per (sequence, head)
+    (40, [1, 40, 3, 9, 33]),           # four wavefronts per pair (some with one split or none)
+])
+def test_lse_combine_alone(gpu, S, ns):
     import torch
-    rng = np.random.default_rng(3)
-    B, S, Hq, D = 5, 6, 4, 128
+    rng = np.random.default_rng(3 + S)
+    B, Hq, D = 5, 4, 128
     o = rng.standard_normal((B, S, Hq, D)).astype(np.float32)
     l = rng.standard_normal((B, S, Hq)).astype(np.float32) * 3
-    ns = np.array([1, 6, 3, 2, 6], np.int32)
+    ns = np.array(ns, np.int32)
     l[1, 2] = -np.inf
-    l[3, :2, 0] = -np.inf        # all live splits empty for (3, head 0)
-    G.announce("lse_combine")
+    l[3, :ns[3], 0] = -np.inf      # all live splits empty for (3, head 0)
+    l[4, ns[4] - 1, 1] = 40.0      # one split far above the others of (4, head 1)
+    G.announce(f"lse_combine S={S}")
     out, lse = G.pkv.lse_combine(torch.from_numpy(o).to(gpu), torch.from_numpy(l).to(gpu), G.ints(ns, gpu))
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     for b in range(B):
@@ -304,6 +309,28 @@ def test_lse_combine_alone(gpu):
             ro, rl = O.oracle.lse_combine(o[b, :ns[b], h].astype(np.float64), l[b, :ns[b], h].astype(np.float64))
             assert O.compare(out[b, h], ro, atol=1e-5, rtol=1e-5)["ok"], (b, h)
             assert (rl == -np.inf and lse[b, h] == -np.inf) or abs(lse[b, h] - rl) < 1e-5
+
+
+@pytest.mark.parametrize("S", [6, 40])
+def test_lse_combine_nan_and_bad_split_counts(gpu, S):
+    """A NaN lse among a pair's live splits makes that pair NaN; a split count
+    outside [1, S] makes the whole sequence NaN; the rest are untouched."""
+    import torch
+    rng = np.random.default_rng(11 + S)
+    B, Hq, D = 4, 4, 128
+    o = rng.standard_normal((B, S, Hq, D)).astype(np.float32)
+    l = rng.standard_normal((B, S, Hq)).astype(np.float32)
+    ns = np.array([S, 0, S + 1, 2], np.int32)
+    l[0, S - 1, 2] = np.nan
+    G.announce(f"lse_combine NaN S={S}")
+    out, lse = G.pkv.lse_combine(torch.from_numpy(o).to(gpu), torch.from_numpy(l).to(gpu), G.ints(ns, gpu))
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.isnan(out[0, 2]).all() and np.isnan(lse[0, 2])
+    assert np.isnan(out[1]).all() and np.isnan(out[2]).all() and np.isnan(lse[1]).all() and np.isnan(lse[2]).all()
+    for b, h in [(0, 0), (0, 1), (0, 3), (3, 0), (3, 3)]:
+        ro, rl = O.oracle.lse_combine(o[b, :ns[b], h].astype(np.float64), l[b, :ns[b], h].astype(np.float64))
+        assert O.compare(out[b, h], ro, atol=1e-5, rtol=1e-5)["ok"], (b, h)
+        assert abs(lse[b, h] - rl) < 1e-5
 
 
 def test_bad_device_metadata_gives_nan_not_a_fault(gpu):
