@@ -562,7 +562,6 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
   if (q_dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "%s: q_dtype=%s (built: BF16)", fn, dtype_name(q_dtype));
   if (cache->kv_dtype == PKV_F32)
     return fail(PKV_ERR_UNSUPPORTED, "%s: F32 cache (built: BF16, I8, FP8)", fn);
-  if (cache->head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim=%d (built: 128)", fn, cache->head_dim);
   if (q == nullptr || cu_q_lens == nullptr || block_tables == nullptr || context_lens == nullptr || out == nullptr)
     return fail(PKV_ERR_INVALID_ARG, "%s: q/cu_q_lens/block_tables/context_lens/out is NULL", fn);
   if (!aligned16(q) || !aligned16(out)) return fail(PKV_ERR_INVALID_ARG, "%s: q/out not 16-byte aligned", fn);
@@ -597,9 +596,10 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
   dr.max_q_len = max_q_len;
   if (pkv_status st = debug_validate(fn, dr, stream); st != PKV_OK) return st;
   const int group = num_q_heads / cache->num_kv_heads;
-  if (static_cast<int64_t>(max_q_len) * group <= kRowsMfmaMax) {
+  if (static_cast<int64_t>(max_q_len) * group <= kRowsMfmaMax && cache->head_dim == 128) {
     // chunks of a few rows (speculative verification): the decode kernels,
-    // with every chunk row of a kv head's query heads on each K/V tile
+    // with every chunk row of a kv head's query heads on each K/V tile (head
+    // dims of 64 take the chunk kernel below for every chunk length)
     pkv::DecodeParams dp{};
     dp.q = q;
     dp.k = cache->k;

@@ -65,24 +65,21 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 
-constexpr int kD = 128;            // head_dim built
 constexpr int kRows = 128;         // query rows per workgroup
 constexpr int kTile = 64;          // tokens per KV tile
 constexpr int kThreads = 512;
 constexpr int kXcdsC = 8;
 constexpr int kStages = 3;
-constexpr int kKBytes = kTile * kD * 2;    // 16 KiB, row-major [token][dim], swizzled
-constexpr int kVBytes = kD * kTile * 2;    // 16 KiB, transposed [dim][token], swizzled
-static_assert(kKBytes == kVBytes, "K and V^T stages of one size");
 constexpr int kIdsCached = 4096;           // block ids kept in LDS (65536 tokens)
 constexpr int kRsrcWord3 = 0x00020000;     // buffer descriptor word 3 (gfx9 family): raw dwords
-constexpr int kMergeFloats = 66;           // per lane of a merging wavefront: o[64], m, l
 
 // Row order of the S^T product: bits 2 and 3 of the row index swapped.
 __device__ __forceinline__ int sigma(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
-// K row t, 16-byte unit u (8 dims). The XOR key sigma(t) makes the 16 lanes
-// of one operand read (rows sigma(0..15), one unit) hit 16 different units.
-__device__ __forceinline__ int k_off(int t, int u) { return t * 256 + ((u ^ (sigma(t) & 15)) << 4); }
+// K row t (D dims, 2 D bytes), 16-byte unit u (8 dims). The XOR key sigma(t)
+// makes the lanes of one operand read (rows sigma(0..15), one unit) hit
+// different units.
+template <int D>
+__device__ __forceinline__ int k_off(int t, int u) { return t * (2 * D) + ((u ^ (sigma(t) & (D / 8 - 1))) << 4); }
 // V^T row d (one dim: 64 tokens = 8 units of 8 tokens).
 __device__ __forceinline__ int vt_sw(int d) { return (d ^ (d >> 3) ^ (d >> 6)) & 7; }
 __device__ __forceinline__ int vt_off(int d, int u) { return d * 128 + ((u ^ vt_sw(d)) << 4); }
@@ -176,10 +173,12 @@ __device__ __forceinline__ void lds_write4(uint32_t a, int off, uint32_t x) {
 
 // One tile's global loads for one thread, held in registers until they are
 // stored to LDS. A thread stages part of its group's 32-token half of the
-// tile: tg = (thread % 256) / 16, u = thread % 16.
+// tile: unit u = (thread % 256) % (D / 8) of K token tg + (2048 / D) i
+// (chunk i, tg = (thread % 256) / (D / 8)), and of V tokens 2 tp, 2 tp + 1
+// (tp = tg, for head_dim 64 only the first 128 threads).
 struct Staged {
-  uint4 k[2];      // K chunk i: token tg + 16 i of the half, 16-byte unit u (8-bit codes: 8 bytes)
-  uint4 v[2];      // V: tokens 2 tg and 2 tg + 1 of the half, unit u
+  uint4 k[2];      // K chunk i (head_dim 128: chunks 0, 1; 64: chunk 0), unit u (8-bit codes: 8 bytes)
+  uint4 v[2];      // V: tokens 2 tp and 2 tp + 1 of the half, unit u
   float sc;        // 8-bit codes: the K (thread % 64 < 32) or V scale of token thread % 32 of the half
   bool sc_ok;      // that token exists
 };
@@ -189,8 +188,15 @@ struct Staged {
 // id inside the loop would make the compiler wait for it with vmcnt(0), that
 // is, for every tile load in flight as well (vector memory counts retire in
 // order), and the loads issued for later tiles would lose their lead.
-template <int KV, int G, bool kIdsInLds>
+template <int KV, int G, bool kIdsInLds, int D>
 __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
+  constexpr int kD = D;                      // head_dim
+  constexpr int kKS = D / 16;                // k-steps of the S^T product
+  constexpr int kDB = D / 32;                // 32-dim blocks of O^T
+  constexpr int kUnits = D / 8;              // 16-byte units (8 dims) of a staged row
+  constexpr int kKC = D / 64;                // K chunks a thread stages per half tile
+  constexpr int kKBytes = kTile * D * 2;     // a stage: K row-major [token][dim] or V^T [dim][token], swizzled
+  constexpr int kMergeFloats = D / 2 + 2;    // per lane of a merging wavefront: o[D / 2], m, l
   constexpr int P = kRows / G;               // positions per query tile
   constexpr bool kScaled = is_scaled_kv(KV);   // int8 / fp8 codes + a scale per row
   constexpr float kSlack = 8.0f;
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   // weights that matter stay clear of fp16's subnormal range.
   constexpr float kP16Shift = 4.0f;
   constexpr int kRowBytes = kScaled ? kD : 2 * kD;   // bytes of one cached K or V row
-  constexpr int kUnit = kRowBytes / 16;          // bytes of 8 dims of a cached row
+  constexpr int kUnit = kRowBytes / kUnits;      // bytes of 8 dims of a cached row
   // stages 0 .. 2: K (row-major); stages 3 .. 5: V^T of the same tiles
   __shared__ __attribute__((aligned(16))) char s_kv[2 * kStages][kKBytes];
   __shared__ __attribute__((aligned(16))) float s_sc[kStages][2 * kTile];   // 8-bit codes: K scale x softmax scale, V scale
@@ -255,12 +261,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   const int pos = n - L + pi;                       // this row attends keys t <= pos
 
   // ---- q rows as MFMA B operands (k = dims 16 ks + 8 h .. +7) ----
-  bf16x8_t qb[8];
+  bf16x8_t qb[kKS];
   {
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
                            (static_cast<size_t>(q0 + (row_live ? pi : 0)) * p.num_q_heads + hq) * kD;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < kKS; ++ks) {
       uint4 x = make_uint4(0, 0, 0, 0);
       if (row_live) x = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * h);
       qb[ks] = __builtin_bit_cast(bf16x8_t, x);
@@ -298,19 +304,24 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 
   // Each group of 4 wavefronts (th = 0: wavefronts 0-3, th = 1: 4-7) loads
   // and stages only the 32-token half of every tile it computes on, so the
-  // two groups share no staged data. Group-local thread tl: tg = tl / 16
-  // (0 .. 15), u = tl % 16.
+  // two groups share no staged data. Group-local thread tl: tg = tl / (D / 8),
+  // u = tl % (D / 8); the V pair index tp = tg stages V only below 16.
   const int tl = tid & 255;
-  const int u16 = tl & 15;
-  const int tg = tl >> 4;
+  const int un = tl % kUnits;
+  const int tg = tl / kUnits;
   const int wl = wu & 3;                            // wavefront within its group
+  // head_dim 64: K chunk 0 of wavefronts 2, 3 is in the group's second block;
+  // V is staged by wavefronts 0 (block 0) and 1 (block 1) only
+  const bool has_v = kD == 128 || wl < 2;
+  const int vblk = kD == 128 ? (wl >> 1) : (wl & 1);
   const char* kpool = static_cast<const char*>(p.k);
   const char* vpool = static_cast<const char*>(p.v);
 
   // Where tile `tile`'s loads come from: buffer descriptors over the valid
   // rows of this wavefront's blocks (none for blocks the range does not
   // need) and this thread's scale. K chunk i comes from block 2 th + i
-  // (row tg), V from block 2 th + wl / 2. Any tile index is safe.
+  // (head_dim 64: block 2 th + wl / 2), row tg % 16; V from block
+  // 2 th + vblk. Any tile index is safe.
   struct TileSrc {
     __amdgpu_buffer_rsrc_t k[2];
     __amdgpu_buffer_rsrc_t v;
@@ -342,10 +353,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     int rk0, rk1;
     const int id0 = block_src(blk0, rk0);
     const int id1 = block_src(blk0 + 1, rk1);
-    ts.k[0] = rsrc(kpool + head_off + id0 * blk_stride, rk0 * kRowBytes);
-    ts.k[1] = rsrc(kpool + head_off + id1 * blk_stride, rk1 * kRowBytes);
-    const bool v1 = (wl >> 1) != 0;
-    ts.v = rsrc(vpool + head_off + (v1 ? id1 : id0) * blk_stride, (v1 ? rk1 : rk0) * kRowBytes);
+    if constexpr (kKC == 2) {
+      ts.k[0] = rsrc(kpool + head_off + id0 * blk_stride, rk0 * kRowBytes);
+      ts.k[1] = rsrc(kpool + head_off + id1 * blk_stride, rk1 * kRowBytes);
+    } else {
+      const bool k1 = (wl >> 1) != 0;
+      ts.k[0] = rsrc(kpool + head_off + (k1 ? id1 : id0) * blk_stride, (k1 ? rk1 : rk0) * kRowBytes);
+    }
+    const bool v1 = vblk != 0;
+    ts.v = rsrc(vpool + head_off + (v1 ? id1 : id0) * blk_stride, has_v ? (v1 ? rk1 : rk0) * kRowBytes : 0);
     if constexpr (kScaled) {
       // scale of token 32 th + (tl % 32): K for tl % 64 < 32, V otherwise
       const int t = tl & 31;
@@ -355,20 +371,24 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     }
   };
   // The loads themselves: the same 4 (+1 scale) loads for every tile, no branch.
-  const int koff = tg * kRowBytes + u16 * kUnit;                   // K chunk i: row tg of block 2 th + i
-  const int voff = ((2 * tg) & 15) * kRowBytes + u16 * kUnit;      // V: rows 2 tg % 16, + 1
+  const int koff = (tg & 15) * kRowBytes + un * kUnit;             // K chunk i: row tg % 16 of its block
+  const int voff = ((2 * tg) & 15) * kRowBytes + un * kUnit;       // V: rows 2 tp % 16, + 1
   auto gissue = [&](const TileSrc& ts, Staged& st) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if constexpr (kScaled) {
-        const u32x2v_t c = __builtin_bit_cast(u32x2v_t, __builtin_amdgcn_raw_buffer_load_b64(ts.k[i], koff, 0, 0));
-        st.k[i] = make_uint4(c.x, c.y, 0, 0);
+        if (i < kKC) {
+          const u32x2v_t c = __builtin_bit_cast(u32x2v_t, __builtin_amdgcn_raw_buffer_load_b64(ts.k[i], koff, 0, 0));
+          st.k[i] = make_uint4(c.x, c.y, 0, 0);
+        }
         const u32x2v_t d = __builtin_bit_cast(
             u32x2v_t, __builtin_amdgcn_raw_buffer_load_b64(ts.v, voff + i * kRowBytes, 0, 0));
         st.v[i] = make_uint4(d.x, d.y, 0, 0);
       } else {
-        const u32x4v_t c = __builtin_bit_cast(u32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(ts.k[i], koff, 0, 0));
-        st.k[i] = make_uint4(c.x, c.y, c.z, c.w);
+        if (i < kKC) {
+          const u32x4v_t c = __builtin_bit_cast(u32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(ts.k[i], koff, 0, 0));
+          st.k[i] = make_uint4(c.x, c.y, c.z, c.w);
+        }
         const u32x4v_t d = __builtin_bit_cast(
             u32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(ts.v, voff + i * kRowBytes, 0, 0));
         st.v[i] = make_uint4(d.x, d.y, d.z, d.w);
@@ -387,11 +407,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 
   // LDS byte offsets of this thread's stores, the same for every stage
   const uint32_t k_lds = lds_address(&s_kv[0][0]), v_lds = lds_address(&s_kv[kStages][0]);
-  const uint32_t kw_a = lane_address(k_lds + k_off(32 * th + tg, u16));   // K chunk i: token 32 th + tg + 16 i, + 4096 i
-  // V^T: dims 8 u + e, tokens 32 th + 2 tg, + 1 (4 bytes in unit 4 th + tg / 4)
+  // K chunk i: token 32 th + tg + 16 i, at + 32 D i bytes
+  const uint32_t kw_a = lane_address(k_lds + k_off<kD>(32 * th + tg, un));
+  // V^T: dims 8 u + e, tokens 32 th + 2 tp, + 1 (4 bytes in unit 4 th + tp / 4)
   uint32_t vw_a[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) vw_a[e] = lane_address(v_lds + vt_off(8 * u16 + e, 4 * th + (tg >> 2)) + ((tg & 3) << 2));
+  for (int e = 0; e < 8; ++e)
+    vw_a[e] = lane_address(v_lds + vt_off(has_v ? 8 * un + e : 0, 4 * th + ((tg & 15) >> 2)) + ((tg & 3) << 2));
 
   // K chunk i of st -> bf16 (8-bit codes converted)
   auto k_bf16 = [&](const Staged& st, int i) -> uint4 {
@@ -451,22 +473,24 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   auto lstore = [&](const Staged& st, int stage) {
     const int so = stage * kKBytes;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) lds_write16(kw_a, so + 4096 * i, k_bf16(st, i));
-    uint32_t vw[2][4];
-    v_prep(st, vw);
+    for (int i = 0; i < kKC; ++i) lds_write16(kw_a, so + 32 * kD * i, k_bf16(st, i));
+    if (has_v) {
+      uint32_t vw[2][4];
+      v_prep(st, vw);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) lds_write4(vw_a[e], so, v_word(st, vw, e));
+      for (int e = 0; e < 8; ++e) lds_write4(vw_a[e], so, v_word(st, vw, e));
+    }
     sc_store(st, stage);
   };
 
   // LDS byte offsets of this lane's MFMA operand reads, the same for every stage
   const int ar = lane & 31;
-  uint32_t kr_a[8];                                 // K row 32 th + sigma(ar), unit 2 ks + h
+  uint32_t kr_a[kKS];                               // K row 32 th + sigma(ar), unit 2 ks + h
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) kr_a[ks] = lane_address(k_lds + k_off(32 * th + sigma(ar), 2 * ks + h));
-  uint32_t vr_a[4][2];                              // V^T row 32 db + ar, unit 2 (2 th + k2) + h
+  for (int ks = 0; ks < kKS; ++ks) kr_a[ks] = lane_address(k_lds + k_off<kD>(32 * th + sigma(ar), 2 * ks + h));
+  uint32_t vr_a[kDB][2];                            // V^T row 32 db + ar, unit 2 (2 th + k2) + h
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < kDB; ++db) {
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) vr_a[db][k2] = lane_address(v_lds + vt_off(32 * db + ar, 2 * (2 * th + k2) + h));
   }
@@ -476,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     const int so = stage * kKBytes;
     s = f32x16_t{};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < kKS; ++ks) {
       const uint4 a = lds_read16(kr_a[ks], so);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qb[ks], s, 0, 0, 0);
     }
@@ -485,9 +509,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   // ---- online softmax state of this lane's row, over this wavefront's tokens ----
   float m = neg_inf(), l = 0.f;
   float mu_off = 0.f;   // 8-bit caches: kP16Shift + lvs, set before the loop
-  f32x16_t o[4];
+  f32x16_t o[kDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
+  for (int db = 0; db < kDB; ++db) o[db] = f32x16_t{};
   f32x16_t sacc;   // S^T of the tile being softmaxed
   bf16x8_t phi[2], plo[2];   // P^T of that tile: bf16 high parts and residuals (8-bit caches: fp16 in phi)
 
@@ -516,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     f32x16_t sn = f32x16_t{};
     auto mfma1 = [&](int ks) {
       sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks % 3]), qb[ks], sn, 0, 0, 0);
-      if (ks + 3 < 8) ka[ks % 3] = lds_read16(kr_a[ks + 3], so);
+      if (ks + 3 < kKS) ka[ks % 3] = lds_read16(kr_a[ks + 3], so);
     };
     // slots 0-3: scale, mask and max of scores 4 c .. 4 c + 3
     float cmax = neg_inf();
@@ -554,7 +578,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     uint32_t pw_hi[8], pw_lo[8];   // P^T words: registers 2 k, 2 k + 1
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      mfma1(4 + c);
+      if (4 + c < kKS) mfma1(4 + c);
       if (c == 0) {
         float tmax = xor32_max(cmax);
         if constexpr (!kScaled) tmax *= p.scale_log2;   // the max commutes with a positive scale
@@ -605,7 +629,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     }
     if (wave_any(corr != 1.f)) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= corr;
+      for (int db = 0; db < kDB; ++db) o[db] *= corr;
     }
     sacc = sn;   // S^T of tile j + 1 (garbage past the last tile, unused)
   };
@@ -617,41 +641,48 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   auto phase2 = [&](int j, int sv_stage, int st_stage, Staged& st, const TileSrc& ns) {
     const int vo = sv_stage * kKBytes;   // V^T stage read
     const int wo = st_stage * kKBytes;   // stage written
-    uint4 va[2][4];
+    uint4 va[2][kDB];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) va[0][db] = lds_read16(vr_a[db][0], vo);
+    for (int db = 0; db < kDB; ++db) va[0][db] = lds_read16(vr_a[db][0], vo);
     uint32_t vw[2][4];
-    // slot s: k-step k2 = s / 4. A bf16 cache: (s % 4) = high part of dims
-    // blocks 0,1 / 2,3, then the residual of 0,1 / 2,3. 8-bit caches: one
-    // fp16 MFMA on dims block s % 4.
+    // slot s: k-step k2 = s / 4. A bf16 cache: (s % 4) = high part of the
+    // first / second half of the dims blocks, then the residual of the first /
+    // second half. 8-bit caches: one fp16 MFMA on dims block s % 4 (head_dim
+    // 64: on block (s % 4) / 2, in the even slots).
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
       const int k2 = sl >> 2, q = sl & 3;
       if (sl == 0) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) va[1][db] = lds_read16(vr_a[db][1], vo);
+        for (int db = 0; db < kDB; ++db) va[1][db] = lds_read16(vr_a[db][1], vo);
       }
       if constexpr (kScaled) {
-        o[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, va[k2][q]),
-                                                      __builtin_bit_cast(f16x8_t, phi[k2]), o[q], 0, 0, 0);
+        constexpr int kEvery = 4 / kDB;
+        if (sl % kEvery == 0) {
+          const int db = q / kEvery;
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, va[k2][db]),
+                                                         __builtin_bit_cast(f16x8_t, phi[k2]), o[db], 0, 0, 0);
+        }
       } else {
         const bf16x8_t b = (q < 2) ? phi[k2] : plo[k2];
 #pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2) {
-          const int db = 2 * (q & 1) + d2;
+        for (int d2 = 0; d2 < kDB / 2; ++d2) {
+          const int db = (kDB / 2) * (q & 1) + d2;
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va[k2][db]), b, o[db], 0, 0, 0);
         }
       }
       // staging of tile j + 2 (st -> LDS stage st_stage), then tile j + 3's loads
       if (sl < 2) {
-        lds_write16(kw_a, wo + 4096 * sl, k_bf16(st, sl));
+        if (sl < kKC) lds_write16(kw_a, wo + 32 * kD * sl, k_bf16(st, sl));
       } else if (sl == 2) {
-        v_prep(st, vw);
+        if (has_v) v_prep(st, vw);
       } else if (sl < 7) {
+        if (has_v) {
 #pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-          const int e = 2 * (sl - 3) + e2;
-          lds_write4(vw_a[e], wo, v_word(st, vw, e));
+          for (int e2 = 0; e2 < 2; ++e2) {
+            const int e = 2 * (sl - 3) + e2;
+            lds_write4(vw_a[e], wo, v_word(st, vw, e));
+          }
         }
       } else {
         sc_store(st, st_stage);
@@ -761,19 +792,20 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   bad = __syncthreads_or(bad);   // also: every wavefront is done with the stages
   // the exponent o and l are taken relative to (8-bit caches: with the V scale reference)
   const float mref = (kScaled && m != neg_inf()) ? m + mu_off : m;
-  float* mb = reinterpret_cast<float*>(&s_kv[0][0]) + (rb * kMergeFloats) * 64 + lane;   // [rb][66][64 lanes]
+  constexpr int kMO = 16 * kDB;   // o values per lane
+  float* mb = reinterpret_cast<float*>(&s_kv[0][0]) + (rb * kMergeFloats) * 64 + lane;   // [rb][o, m, l][64 lanes]
   if (th == 1) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < kDB; ++db) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) mb[(16 * db + v) * 64] = o[db][v];
     }
-    mb[64 * 64] = mref;
-    mb[65 * 64] = l;
+    mb[kMO * 64] = mref;
+    mb[(kMO + 1) * 64] = l;
   }
   __syncthreads();
   if (th == 1 || !row_live) return;
-  const float m2 = mb[64 * 64], l2 = mb[65 * 64];
+  const float m2 = mb[kMO * 64], l2 = mb[(kMO + 1) * 64];
   const float mm = fmaxf(mref, m2);
   const float a1 = (mref == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mref - mm);
   const float a2 = (m2 == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
@@ -782,7 +814,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
 
   // ---- write: lane holds dims 32 db + 8 (v / 4) + 4 h + v % 4 of its row ----
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < kDB; ++db) {
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
       float y[4];
@@ -802,7 +834,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   }
 }
 
-template <int KV, int G>
+template <int KV, int G, int D>
 hipError_t launch_t(const ChunkedParams& p, hipStream_t st) {
   constexpr int P = kRows / G;
   const int QT = (p.max_q_len + P - 1) / P;
@@ -810,31 +842,37 @@ hipError_t launch_t(const ChunkedParams& p, hipStream_t st) {
   if (items > (int64_t(1) << 30)) return hipErrorInvalidValue;
   const int grid = static_cast<int>((items + kXcdsC - 1) / kXcdsC * kXcdsC);
   if (p.max_blocks <= kIdsCached) {
-    hipLaunchKernelGGL((chunked_kernel<KV, G, true>), dim3(grid), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((chunked_kernel<KV, G, true, D>), dim3(grid), dim3(kThreads), 0, st, p);
   } else {
-    hipLaunchKernelGGL((chunked_kernel<KV, G, false>), dim3(grid), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((chunked_kernel<KV, G, false, D>), dim3(grid), dim3(kThreads), 0, st, p);
   }
   return hipGetLastError();
 }
 
-template <int KV>
+template <int KV, int D>
 hipError_t launch_g(const ChunkedParams& p, int group, hipStream_t st) {
   switch (group) {
-    case 1: return launch_t<KV, 1>(p, st);
-    case 2: return launch_t<KV, 2>(p, st);
-    case 4: return launch_t<KV, 4>(p, st);
-    case 8: return launch_t<KV, 8>(p, st);
+    case 1: return launch_t<KV, 1, D>(p, st);
+    case 2: return launch_t<KV, 2, D>(p, st);
+    case 4: return launch_t<KV, 4, D>(p, st);
+    case 8: return launch_t<KV, 8, D>(p, st);
     default: return hipErrorNotSupported;
   }
+}
+
+template <int KV>
+hipError_t launch_d(const ChunkedParams& p, int head_dim, int group, hipStream_t st) {
+  if (head_dim == 128) return launch_g<KV, 128>(p, group, st);
+  if (head_dim == 64) return launch_g<KV, 64>(p, group, st);
+  return hipErrorNotSupported;
 }
 
 }  // namespace
 
 hipError_t launch_chunked(const ChunkedParams& p, int kv_dtype, int head_dim, int group, hipStream_t st) {
-  if (head_dim != kD) return hipErrorNotSupported;
-  if (kv_dtype == PKV_BF16) return launch_g<PKV_BF16>(p, group, st);
-  if (kv_dtype == PKV_I8) return launch_g<PKV_I8>(p, group, st);
-  if (kv_dtype == PKV_FP8) return launch_g<PKV_FP8>(p, group, st);
+  if (kv_dtype == PKV_BF16) return launch_d<PKV_BF16>(p, head_dim, group, st);
+  if (kv_dtype == PKV_I8) return launch_d<PKV_I8>(p, head_dim, group, st);
+  if (kv_dtype == PKV_FP8) return launch_d<PKV_FP8>(p, head_dim, group, st);
   return hipErrorNotSupported;
 }
 

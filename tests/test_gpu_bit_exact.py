@@ -81,8 +81,8 @@ def _stored_rows(pool, table_row, n):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
-@pytest.mark.parametrize("Hq,Hkv", [(16, 8), (16, 4)])
-def test_chunked_one_hot_rows_before_on_and_after_the_hot_key(gpu, kv, Hq, Hkv):
+@pytest.mark.parametrize("Hq,Hkv,D", [(16, 8, 128), (16, 4, 128), (16, 8, 64)])
+def test_chunked_one_hot_rows_before_on_and_after_the_hot_key(gpu, kv, Hq, Hkv, D):
     """Every sequence holds a warm key at token 0 and one hot key at token j;
     all other keys are zero. Chunk rows at positions before j see only the
     warm key (out == V_0); the row on j and the rows after it see the hot
@@ -91,7 +91,6 @@ def test_chunked_one_hot_rows_before_on_and_after_the_hot_key(gpu, kv, Hq, Hkv):
     high part (1.0) and residual (0); 8-bit caches on fp16 weights with the
     V scale folded in, exact here because the V scales are powers of two."""
     import torch
-    D = 128
     ctx, ql, hot = [300, 200, 130], [200, 64, 130], [128, 170, 129]
     step = W.make_step(f"ch1hot_{kv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, kv_dtype=kv,
                        src_dtype="bf16", seed=300)

@@ -58,6 +58,28 @@ def test_chunked_group_sizes(gpu, kv, Hq, Hkv):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (8, 1), (4, 4), (16, 2)])
+def test_chunked_head_dim_64(gpu, kv, Hq, Hkv):
+    """head_dim 64 (the 128-row kernel over 64-dim rows): ragged chunks and
+    prefixes, a chunk of exactly one tile, and chunks of a few rows (one-row
+    chunks among them), which a head_dim 64 cache also sends to this kernel."""
+    import torch
+    ctx = [200, 77, 1, 130, 64, 300, 9, 1000]
+    ql = [70, 77, 1, 65, 64, 3, 2, 129]
+    step = W.make_step(f"d64_{kv}_{Hq}_{Hkv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=64, kv_dtype=kv,
+                       src_dtype="bf16", seed=700 + Hq + Hkv)
+    cache = G.build_cache(step, gpu)
+    q, cu, tables, cc = step.q, step.cu_q_lens, step.block_tables, step.context_lens
+    G.announce(f"chunked head_dim 64 {step.name}")
+    out, lse = G.pkv.paged_attention_chunked(G.tensor(q, "bf16", gpu), G.ints(cu, gpu), max(ql), cache,
+                                             G.ints(tables, gpu), G.ints(cc, gpu), float(step.scale), return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = O.oracle.paged_chunked(O.oracle.decode_rows(q, "bf16"), cu, O.pool(step), tables, cc, step.scale)
+    check(out.cpu().numpy(), ro, "out")
+    check(lse.cpu().numpy(), rl, "lse")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
 @pytest.mark.parametrize("n", [65536, 70000])
 def test_chunked_context_past_the_lds_block_ids(gpu, kv, n):
     """A 65,536-token context fills the 4,096 block ids the kernel keeps in

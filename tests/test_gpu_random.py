@@ -49,7 +49,8 @@ def _chunked_cases(n_cases: int = 16, seed: int = 20261203):
         S = int(rng.integers(1, 5))
         L = rng.integers(2, 201, size=S)                 # (one-row sequences are decode rows)
         prefix = rng.integers(0, 601, size=S)
-        cases.append(dict(id=f"c{i}_g{g}_h{hkv}_{kv}_S{S}", g=g, hkv=hkv, kv=kv,
+        D = 64 if i % 4 == 3 else 128                    # every fourth case over a head_dim 64 cache
+        cases.append(dict(id=f"c{i}_D{D}_g{g}_h{hkv}_{kv}_S{S}", D=D, g=g, hkv=hkv, kv=kv,
                           ctx=[int(a + b) for a, b in zip(prefix, L)], ql=[int(x) for x in L], seed=4000 + i))
     return cases
 
@@ -108,7 +109,7 @@ def test_random_decode(gpu, case):
 @pytest.mark.parametrize("case", CHUNKED, ids=[c["id"] for c in CHUNKED])
 def test_random_chunked(gpu, case):
     step = W.make_step(case["id"], case["ctx"], case["ql"], num_q_heads=case["g"] * case["hkv"],
-                       num_kv_heads=case["hkv"], head_dim=128, kv_dtype=case["kv"], src_dtype="bf16",
+                       num_kv_heads=case["hkv"], head_dim=case["D"], kv_dtype=case["kv"], src_dtype="bf16",
                        seed=case["seed"])
     cache = G.build_cache(step, gpu)
     out, lse = G.run_chunked(step, cache, gpu)
