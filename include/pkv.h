@@ -280,17 +280,17 @@ pkv_status pkv_paged_attention_decode_append(const void* k_new, const void* v_ne
  *   Cache dtypes: BF16, I8 or FP8; head_dim 64 or 128; GQA group size in
  *   {1, 2, 4, 8}.
  *   A chunk longer than max_q_len or than its context yields NaN rows.
- * With head_dim 128, chunks of a few rows per kv head (max_q_len *
- * (num_q_heads / num_kv_heads) = R) run on decode-shaped kernels, one
- * workgroup per (sequence, kv head)
+ * Chunks of a few rows per kv head (max_q_len * (num_q_heads /
+ * num_kv_heads) = R) run on decode-shaped kernels, one workgroup per
+ * (sequence, kv head)
  * streaming the sequence once with every chunk row of the group's query heads
  * against each K/V tile:
  *   R <= 4      : fp32 FMAs and dot products (the decode's arithmetic);
- *   4 < R <= 16 : 16x16 bf16 MFMAs for QK^T and PV, the weights split into a
+ *   4 < R <= 16 : (head_dim 128) 16x16 bf16 MFMAs for QK^T and PV, the weights split into a
  *                 bf16 high part and residual (~2^-17), 8-bit codes converted
  *                 to bf16 exactly;
  * e.g. speculative verification of up to 8 draft rows with 2 query heads per
- * kv head. Longer chunks, and every chunk over a head_dim 64 cache, run on
+ * kv head. Longer chunks (with head_dim 64: from 5 rows per kv head) run on
  * the 128-row MFMA kernel.
  * Arithmetic: QK^T with bf16 MFMA (exact products, fp32 sums); softmax in
  * fp32. The PV product's weights are bf16 pairs (a high part and its

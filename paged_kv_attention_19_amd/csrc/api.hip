@@ -596,10 +596,12 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
   dr.max_q_len = max_q_len;
   if (pkv_status st = debug_validate(fn, dr, stream); st != PKV_OK) return st;
   const int group = num_q_heads / cache->num_kv_heads;
-  if (static_cast<int64_t>(max_q_len) * group <= kRowsMfmaMax && cache->head_dim == 128) {
+  const int64_t rows = static_cast<int64_t>(max_q_len) * group;
+  if (rows <= kRowsDecodeMax || (rows <= kRowsMfmaMax && cache->head_dim == 128)) {
     // chunks of a few rows (speculative verification): the decode kernels,
-    // with every chunk row of a kv head's query heads on each K/V tile (head
-    // dims of 64 take the chunk kernel below for every chunk length)
+    // with every chunk row of a kv head's query heads on each K/V tile (the
+    // MFMA one is built for head dims of 128; with 64, chunks of 5 to 16 rows
+    // per kv head take the chunk kernel below)
     pkv::DecodeParams dp{};
     dp.q = q;
     dp.k = cache->k;
@@ -621,7 +623,7 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
     dp.max_q_len = max_q_len;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (static_cast<int64_t>(max_q_len) * group > kRowsDecodeMax) {
+    if (rows > kRowsDecodeMax) {
       e = pkv::launch_rows_mfma(dp, cache->kv_dtype, cache->head_dim, group, st);
     } else {
       switch (cache->kv_dtype) {

@@ -440,16 +440,22 @@ hipError_t launch_rows_g(const DecodeParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int KV>
-hipError_t launch_rows_kv(const DecodeParams& p, int head_dim, int group, hipStream_t st) {
-  if (head_dim != 128) return hipErrorInvalidValue;
+template <int KV, int D>
+hipError_t launch_rows_d(const DecodeParams& p, int group, hipStream_t st) {
   switch (group) {
-    case 1: return launch_rows_g<KV, 128, 1>(p, st);
-    case 2: return launch_rows_g<KV, 128, 2>(p, st);
-    case 4: return launch_rows_g<KV, 128, 4>(p, st);
-    case 8: return launch_rows_g<KV, 128, 8>(p, st);
+    case 1: return launch_rows_g<KV, D, 1>(p, st);
+    case 2: return launch_rows_g<KV, D, 2>(p, st);
+    case 4: return launch_rows_g<KV, D, 4>(p, st);
+    case 8: return launch_rows_g<KV, D, 8>(p, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int KV>
+hipError_t launch_rows_kv(const DecodeParams& p, int head_dim, int group, hipStream_t st) {
+  if (head_dim == 128) return launch_rows_d<KV, 128>(p, group, st);
+  if (head_dim == 64) return launch_rows_d<KV, 64>(p, group, st);
+  return hipErrorInvalidValue;
 }
 
 __device__ __forceinline__ int wave_sum_i32(int x) {

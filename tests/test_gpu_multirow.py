@@ -50,6 +50,32 @@ def test_few_row_chunks_match_oracle(gpu, kv, Hq, Hkv, ql):
     check(lse.cpu().numpy(), rl, "lse")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
+@pytest.mark.parametrize("Hq,Hkv,ql", [
+    (8, 4, [2, 1, 2, 2, 1, 2]),        # group 2: up to 4 rows per kv head, the decode kernels
+    (4, 4, [4, 3, 1, 4, 4, 2]),        # group 1: up to 4 rows
+    (8, 2, [3, 1, 4, 2, 4, 1]),        # group 4 x up to 4 rows: 16 rows per kv head, the chunk kernel
+])
+def test_few_row_chunks_head_dim_64(gpu, kv, Hq, Hkv, ql):
+    """head_dim 64: chunks of up to 4 rows per kv head run on the decode
+    kernels, longer ones (the MFMA few-row kernel is built for 128) on the
+    chunk kernel; both against the oracle."""
+    import torch
+    ctx = [300, 77, 1025, 8, 129, 2000]
+    step = W.make_step(f"rows64_{kv}_{Hq}_{Hkv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=64,
+                       kv_dtype=kv, src_dtype="bf16", seed=640 + Hkv + max(ql))
+    cache = G.build_cache(step, gpu)
+    q, cu, tables, cc = step.q, step.cu_q_lens, step.block_tables, step.context_lens
+    G.announce(f"few-row chunks head_dim 64 {step.name}")
+    out, lse = G.pkv.paged_attention_chunked(G.tensor(q, "bf16", gpu), G.ints(cu, gpu), max(ql), cache,
+                                             G.ints(tables, gpu), G.ints(cc, gpu), float(step.scale),
+                                             return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = O.oracle.paged_chunked(O.oracle.decode_rows(q, "bf16"), cu, O.pool(step), tables, cc, step.scale)
+    check(out.cpu().numpy(), ro, "out")
+    check(lse.cpu().numpy(), rl, "lse")
+
+
 def test_spec_verify_shape_matches_oracle(gpu):
     """The benchmark's verification shape: 32 sequences of 128..384 tokens,
     4 new rows each, Qwen3 heads, bf16 (8 rows per kv head: the MFMA kernel)."""

@@ -69,7 +69,8 @@ def _few_row_cases(n_cases: int = 12, seed: int = 20261204):
         lmax = int(rng.integers(1, 16 // g + 1))
         L = rng.integers(1, lmax + 1, size=S)
         prefix = rng.integers(0, 900, size=S)
-        cases.append(dict(id=f"r{i}_g{g}_h{hkv}_{kv}_S{S}_L{int(L.max())}", g=g, hkv=hkv, kv=kv,
+        D = 64 if i % 3 == 2 else 128                    # every third case over a head_dim 64 cache
+        cases.append(dict(id=f"r{i}_D{D}_g{g}_h{hkv}_{kv}_S{S}_L{int(L.max())}", D=D, g=g, hkv=hkv, kv=kv,
                           ctx=[int(a + b) for a, b in zip(prefix, L)], ql=[int(x) for x in L], seed=5000 + i))
     return cases
 
@@ -122,7 +123,7 @@ def test_random_chunked(gpu, case):
 def test_random_few_row_chunks(gpu, case):
     import torch
     step = W.make_step(case["id"], case["ctx"], case["ql"], num_q_heads=case["g"] * case["hkv"],
-                       num_kv_heads=case["hkv"], head_dim=128, kv_dtype=case["kv"], src_dtype="bf16",
+                       num_kv_heads=case["hkv"], head_dim=case["D"], kv_dtype=case["kv"], src_dtype="bf16",
                        seed=case["seed"])
     cache = G.build_cache(step, gpu)
     # every sequence's rows as one chunk (one-row chunks included)
