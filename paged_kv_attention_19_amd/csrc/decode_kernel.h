@@ -821,18 +821,30 @@ hipError_t launch_balanced_t(const DecodeParams& p, int workgroups, hipStream_t 
 }
 
 // waves: wavefronts per workgroup. Each wavefront keeps one block of K/V in
-// flight while it reduces the previous one. Measured on MI355X (16/8 heads,
-// head_dim 128), per step with one block ahead against two: the 32-sequence
-// bf16 step of 128..384 tokens 10.07 against 10.50 us, the mixed step's int8
-// rows 106.9 against 113.4 us, and 8 x 32k bf16 tokens 174.3 against 171.6
-// us. The host sees only the table width, which does not tell these apart,
-// so one block ahead is kept.
+// flight while it reduces the previous one, or two over a bf16 cache whose
+// sequences are cut into kDeepRingSplits or more splits. Measured on MI355X
+// (16/8 heads, head_dim 128), per step with one block ahead against two: the
+// 32-sequence bf16 step of 128..384 tokens (one split each) 10.07 against
+// 10.50 us, the mixed step's int8 rows (1024-token splits, up to 4 per
+// sequence) 106.9 against 113.4 us, and 8 x 32k bf16 tokens in 64 splits
+// 170.7 against 168.2 us. While every wavefront of the chip streams, HBM is
+// oversubscribed and a deeper ring only lengthens the queues, except where
+// each wavefront streams many blocks of a long context, which many splits
+// per sequence mark (the table width does not: a wide table may hold short
+// sequences). An 8-bit cache's blocks carry more VALU work per byte, and its
+// wavefronts lose with the deeper ring even then.
+constexpr int kDeepRingSplits = 8;
+
 template <int KV, int QT, int D, int G>
 hipError_t launch_partial_w(const DecodeParams& p, int waves, hipStream_t st) {
   if (waves < 0) return launch_balanced_t<KV, QT, D, G>(p, -waves, st);   // balanced: -workgroups
   switch (waves) {
     case 2: return launch_partial_t<KV, QT, D, G, 2, 1>(p, st);
-    case 4: return launch_partial_t<KV, QT, D, G, 4, 1>(p, st);
+    case 4:
+      if constexpr (KV == PKV_BF16) {
+        if (!p.direct && p.max_ns >= kDeepRingSplits) return launch_partial_t<KV, QT, D, G, 4, 2>(p, st);
+      }
+      return launch_partial_t<KV, QT, D, G, 4, 1>(p, st);
     case 8: return launch_partial_t<KV, QT, D, G, 8, 1>(p, st);
     default: return hipErrorInvalidValue;
   }

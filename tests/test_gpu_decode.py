@@ -229,6 +229,43 @@ def test_every_split_count_agrees(gpu):
         check(lse, rl, f"lse ns={ns}")
 
 
+@pytest.mark.parametrize("D,G_,qd", [(128, 2, "bf16"), (64, 4, "f32"), (128, 8, "bf16"), (64, 1, "bf16")])
+def test_deep_ring_many_splits(gpu, D, G_, qd):
+    """bf16 caches cut into 8 or more splits per sequence stream with two
+    blocks in flight per wavefront (one otherwise). Against the oracle, with
+    splits from whole blocks down to empty ones; and the split partials bit
+    for bit against the same splits launched with a split bound of 7 (one
+    block in flight): the ring depth changes when loads are issued, not the
+    arithmetic. (The combined outputs may differ in rounding: from 8 splits
+    on, the combine sums them over four wavefronts.)"""
+    Hkv = 2
+    ctx = [1, 16, 17, 129, 700, 2049, 3000]
+    ns = [8, 8, 9, 12, 16, 20, 11]
+    step = W.make_step(f"deep{D}_{G_}", ctx, [1] * len(ctx), num_q_heads=Hkv * G_, num_kv_heads=Hkv, head_dim=D,
+                       q_dtype=qd, kv_dtype="bf16", src_dtype="bf16", num_splits=ns, seed=70 + D + G_)
+    cache = G.build_cache(step, gpu)
+    out, lse = G.run_decode(step, cache, gpu, max_num_splits=20)
+    ro, rl = O.decode(step, O.pool(step))
+    check(out, ro, "out")
+    check(lse, rl, "lse")
+    few = [min(7, n) for n in ns]
+    o8, _ = G.run_decode(step, cache, gpu, num_splits=few, max_num_splits=8)
+    check(o8, ro, "out, 8-split bound")
+    q, tables, ctxs, _ = step.decode_batch()
+    parts = {}
+    for bound in (7, 8):
+        ws = G.torch.zeros(G.pkv.decode_workspace_bytes(len(ctx), step.num_q_heads, D, bound), dtype=G.torch.uint8,
+                           device=gpu)
+        op, lp = G.pkv.paged_attention_decode(G.tensor(q, step.q_dtype, gpu), cache, G.ints(tables, gpu),
+                                              G.ints(ctxs, gpu), G.ints(np.asarray(few, np.int32), gpu), bound,
+                                              float(step.scale), workspace=ws, partials_only=True)
+        G.torch.cuda.synchronize()
+        parts[bound] = (op.cpu().numpy(), lp.cpu().numpy())
+    for b, k in enumerate(few):
+        assert np.array_equal(parts[8][0][b, :k].view(np.uint32), parts[7][0][b, :k].view(np.uint32)), b
+        assert np.array_equal(parts[8][1][b, :k].view(np.uint32), parts[7][1][b, :k].view(np.uint32)), b
+
+
 # ---------------------------------------------------------------------------
 # indexing: bit-exact probes
 # ---------------------------------------------------------------------------
