@@ -379,8 +379,7 @@ struct WaveDecoder {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float mm = m[g];
-#pragma unroll
-      for (int msk = LPT; msk < kWave; msk <<= 1) mm = fmaxf(mm, __shfl_xor(mm, msk));
+      mm = coset_reduce<LPT>(mm, OpMax{});
       M[g] = mm;
       const float a = (m[g] == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(m[g] - mm);
       l[g] *= a;
@@ -394,13 +393,10 @@ struct WaveDecoder {
   // wavefront's total (l and acc); lanes 0 .. LPT-1 then hold all D dims.
   __device__ __forceinline__ void sum_slots() {
 #pragma unroll
-    for (int msk = LPT; msk < kWave; msk <<= 1) {
+    for (int g = 0; g < G; ++g) {
+      l[g] = coset_reduce<LPT>(l[g], OpAdd{});
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        l[g] += __shfl_xor(l[g], msk);
-#pragma unroll
-        for (int e = 0; e < NE; ++e) acc[g][e] += __shfl_xor(acc[g][e], msk);
-      }
+      for (int e = 0; e < NE; ++e) acc[g][e] = coset_reduce<LPT>(acc[g][e], OpAdd{});
     }
   }
 

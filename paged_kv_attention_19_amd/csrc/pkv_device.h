@@ -124,6 +124,35 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+// Max / sum of x over the lanes l, l + S, l + 2 S, ... of the wavefront (S a
+// power of two, 1 <= S <= 32): every lane receives the result for its coset
+// l mod S. Within a 16-lane row the steps are DPP row rotations (by S, 2 S,
+// ... 8, which cover the row's lanes of the coset); across rows, gfx950's
+// v_permlane16_swap and v_permlane32_swap, which exchange rows between two
+// registers, so that with x in both each lane sees its own value and the one
+// 16 (32) lanes away: VALU steps, no LDS crossbar round trip.
+constexpr int kDppRowRor1 = 0x121;   // row_ror:1; row_ror:r is kDppRowRor1 + r - 1
+template <int S, typename Op>
+__device__ __forceinline__ float coset_reduce(float x, Op op) {
+  static_assert(S >= 1 && S <= 32 && (S & (S - 1)) == 0, "stride");
+  if constexpr (S <= 1) x = op(x, dpp<kDppRowRor1>(x));
+  if constexpr (S <= 2) x = op(x, dpp<kDppRowRor1 + 1>(x));
+  if constexpr (S <= 4) x = op(x, dpp<kDppRowRor1 + 3>(x));
+  if constexpr (S <= 8) x = op(x, dpp<kDppRowRor1 + 7>(x));
+  if constexpr (S <= 16) {
+    const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  }
+  const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(w[0]), __uint_as_float(w[1]));
+}
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpAdd {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+
 // Sum over aligned groups of W lanes (W in 1,2,4,8,16,32,64); every lane of
 // the group receives the total. Within a 16-lane row the steps are DPP moves;
 // across rows they are LDS-crossbar shuffles.
