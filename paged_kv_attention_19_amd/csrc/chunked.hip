@@ -734,8 +734,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   }
   gload(2, sa);
   if constexpr (kScaled) {
-#pragma unroll
-    for (int x = 1; x < 64; x <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, x));   // NaN ignored
+    vmax = coset_reduce<1>(vmax, OpMax{});   // over the wavefront, by VALU lane exchanges; NaN ignored
     if (lane == 0) s_vmax[w] = vmax;
   }
   __syncthreads();
