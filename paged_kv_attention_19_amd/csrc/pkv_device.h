@@ -153,32 +153,41 @@ struct OpAdd {
   __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
 };
 
-// Sum over aligned groups of W lanes (W in 1,2,4,8,16,32,64); every lane of
-// the group receives the total. Within a 16-lane row the steps are DPP moves;
-// across rows they are LDS-crossbar shuffles.
+// Sum / max over aligned groups of W lanes (W in 1,2,4,8,16,32,64); every
+// lane of the group receives the result. Within a 16-lane row the steps are
+// DPP moves (quad permutes, then the half-row and row mirrors, each of which
+// pairs a lane with one in the other half of its group); across rows,
+// v_permlane16_swap and v_permlane32_swap. Every step combines two values
+// with a commutative operation, so each lane of a group computes the same
+// bits.
+template <int W, typename Op>
+__device__ __forceinline__ float group_reduce(float x, Op op) {
+  if constexpr (W >= 2) x = op(x, dpp<kDppQuadXor1>(x));
+  if constexpr (W >= 4) x = op(x, dpp<kDppQuadXor2>(x));
+  if constexpr (W >= 8) x = op(x, dpp<kDppRowHalfMirror>(x));
+  if constexpr (W >= 16) x = op(x, dpp<kDppRowMirror>(x));
+  if constexpr (W >= 32) {
+    const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  }
+  if constexpr (W >= 64) {
+    const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(w[0]), __uint_as_float(w[1]));
+  }
+  return x;
+}
+
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
-  if constexpr (W >= 2) x += dpp<kDppQuadXor1>(x);
-  if constexpr (W >= 4) x += dpp<kDppQuadXor2>(x);
-  if constexpr (W >= 8) x += dpp<kDppRowHalfMirror>(x);
-  if constexpr (W >= 16) x += dpp<kDppRowMirror>(x);
-  if constexpr (W >= 32) x += __shfl_xor(x, 16);
-  if constexpr (W >= 64) x += __shfl_xor(x, 32);
-  return x;
+  return group_reduce<W>(x, OpAdd{});
 }
 
 template <int W>
 __device__ __forceinline__ float group_max(float x) {
-#pragma unroll
-  for (int m = 1; m < W; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
+  return group_reduce<W>(x, OpMax{});
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
-}
+__device__ __forceinline__ float wave_max(float x) { return group_reduce<kWave>(x, OpMax{}); }
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_read_exec() & __ballot(p); }
 
