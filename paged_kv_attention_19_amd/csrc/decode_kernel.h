@@ -222,31 +222,33 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeParams p)
   }
   __syncthreads();
 
-  bool any_bad = false;
+  int bad_or = 0;   // no short-circuit: the flags' reads go out together
 #pragma unroll
-  for (int ww = 0; ww < NW; ++ww) any_bad = any_bad || (s_bad[ww] != 0);
+  for (int ww = 0; ww < NW; ++ww) bad_or |= s_bad[ww];
+  const bool any_bad = bad_or != 0;
 
   for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
     const int g = idx / D;
     const int d = idx % D;
+    // No branch on the maxima: every LDS read of the merge can go out at
+    // once. A wavefront with no finite score (mw = -inf) gets weight 0; with
+    // none anywhere, L = 0.
     float Mx = neg_inf();
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) Mx = fmaxf(Mx, s_m[ww][g]);
     float L = 0.f, O = 0.f;
-    if (Mx != neg_inf()) {
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float mw = s_m[ww][g];
-        const float wt = (mw == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
-        float ls = 0.f, os = 0.f;
+    for (int ww = 0; ww < NW; ++ww) {
+      const float mw = s_m[ww][g];
+      const float wt = (mw == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
+      float ls = 0.f, os = 0.f;
 #pragma unroll
-        for (int t = 0; t < kSlots; ++t) {
-          ls += s_lp[ww][t][g];
-          os += s_part[ww][t][g][d];
-        }
-        L += ls * wt;
-        O += os * wt;
+      for (int t = 0; t < kSlots; ++t) {
+        ls += s_lp[ww][t][g];
+        os += s_part[ww][t][g][d];
       }
+      L += ls * wt;
+      O += os * wt;
     }
     float o, lse;
     if (any_bad) {
@@ -376,33 +378,34 @@ __global__ __launch_bounds__(NW * 64) void decode_rows_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  bool any_bad = false;
+  int bad_or = 0;   // no short-circuit: the flags' reads go out together
 #pragma unroll
-  for (int ww = 0; ww < NW; ++ww) any_bad = any_bad || (s_bad[ww] != 0);
+  for (int ww = 0; ww < NW; ++ww) bad_or |= s_bad[ww];
+  const bool any_bad = bad_or != 0;
 
   for (int idx = threadIdx.x; idx < R * D; idx += NW * kWave) {
     const int g = idx / D;
     const int d = idx % D;
     const int r = g / GQ;
     if (r >= L) continue;
+    // no branch on the maxima (as in the decode's merge): weight 0 for a
+    // wavefront with no finite score
     float Mx = neg_inf();
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) Mx = fmaxf(Mx, s_m[ww][g]);
     float Ls = 0.f, O = 0.f;
-    if (Mx != neg_inf()) {
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float mw = s_m[ww][g];
-        const float wt = (mw == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
-        float ls = 0.f, os = 0.f;
+    for (int ww = 0; ww < NW; ++ww) {
+      const float mw = s_m[ww][g];
+      const float wt = (mw == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
+      float ls = 0.f, os = 0.f;
 #pragma unroll
-        for (int t = 0; t < kSlots; ++t) {
-          ls += s_lp[ww][t][g];
-          os += s_part[ww][t][g][d];
-        }
-        Ls += ls * wt;
-        O += os * wt;
+      for (int t = 0; t < kSlots; ++t) {
+        ls += s_lp[ww][t][g];
+        os += s_part[ww][t][g][d];
       }
+      Ls += ls * wt;
+      O += os * wt;
     }
     float o, lse;
     if (any_bad) {
