@@ -324,21 +324,24 @@ def test_output_is_bit_identical_under_block_placement(gpu):
     assert out1.tobytes() == out2.tobytes() and lse1.tobytes() == lse2.tobytes()
 
 
-@pytest.mark.parametrize("S,ns", [
-    (6, [1, 6, 3, 2, 6]),              # one wavefront per (sequence, head)
-    (40, [1, 40, 3, 9, 33]),           # four wavefronts per pair (some with one split or none)
+@pytest.mark.parametrize("S,ns,D", [
+    (6, [1, 6, 3, 2, 6], 128),             # one wavefront per (sequence, head)
+    (40, [1, 40, 3, 9, 33], 128),          # four wavefronts per pair (some with one split or none)
+    (150, [1, 150, 70, 65, 129], 128),     # four wavefronts, several chunks of 16 splits each
+    (150, [2, 149, 70, 66, 150], 64),
 ])
-def test_lse_combine_alone(gpu, S, ns):
+def test_lse_combine_alone(gpu, S, ns, D):
     import torch
-    rng = np.random.default_rng(3 + S)
-    B, Hq, D = 5, 4, 128
+    rng = np.random.default_rng(3 + S + D)
+    B, Hq = 5, 4
     o = rng.standard_normal((B, S, Hq, D)).astype(np.float32)
     l = rng.standard_normal((B, S, Hq)).astype(np.float32) * 3
     ns = np.array(ns, np.int32)
     l[1, 2] = -np.inf
     l[3, :ns[3], 0] = -np.inf      # all live splits empty for (3, head 0)
     l[4, ns[4] - 1, 1] = 40.0      # one split far above the others of (4, head 1)
-    G.announce(f"lse_combine S={S}")
+    l[2, :64, 0] = -np.inf         # with several chunks: the first chunk of every wavefront empty
+    G.announce(f"lse_combine S={S} D={D}")
     out, lse = G.pkv.lse_combine(torch.from_numpy(o).to(gpu), torch.from_numpy(l).to(gpu), G.ints(ns, gpu))
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     for b in range(B):
@@ -348,7 +351,7 @@ def test_lse_combine_alone(gpu, S, ns):
             assert (rl == -np.inf and lse[b, h] == -np.inf) or abs(lse[b, h] - rl) < 1e-5
 
 
-@pytest.mark.parametrize("S", [6, 40])
+@pytest.mark.parametrize("S", [6, 40, 100])
 def test_lse_combine_nan_and_bad_split_counts(gpu, S):
     """A NaN lse among a pair's live splits makes that pair NaN; a split count
     outside [1, S] makes the whole sequence NaN; the rest are untouched."""
