@@ -276,8 +276,7 @@ __global__ __launch_bounds__(NW * 64) void rows_mfma_kernel(DecodeParams p) {
       bm = fmaxf(bm, x[v]);
     }
     if (wave_any(bm > m + kSlack)) {
-      float bmr = fmaxf(bm, __shfl_xor(bm, 16));
-      bmr = fmaxf(bmr, __shfl_xor(bmr, 32));   // the row's max over its four lanes
+      const float bmr = coset_reduce<16>(bm, OpMax{});   // the row's max over its four lanes
       if (bmr > m + kSlack) {
         const float corr = __builtin_amdgcn_exp2f(m - bmr);   // m = -inf -> 0
         lsum *= corr;
@@ -349,8 +348,7 @@ __global__ __launch_bounds__(NW * 64) void rows_mfma_kernel(DecodeParams p) {
   }
 
   // ---- merge the four wavefronts' states through LDS ----
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);   // the row's denominator over this wavefront's tokens
+  lsum = coset_reduce<16>(lsum, OpAdd{});   // the row's denominator over its four lanes (l, l ^ 16, ...)
   if (lane == 0) s_bad[w] = bad ? 1 : 0;
   __syncthreads();   // every wavefront is done with its V^T stages
   float* mo = reinterpret_cast<float*>(&s_vt[0][0][0]);          // [w][row][kD] then [w][row][m, l]
@@ -365,25 +363,26 @@ __global__ __launch_bounds__(NW * 64) void rows_mfma_kernel(DecodeParams p) {
     ml[(w * kRowsN + row) * 2 + 1] = lsum;
   }
   __syncthreads();
-  bool any_bad = false;
+  int bad_or = 0;   // no short-circuit: the flags' reads go out together
 #pragma unroll
-  for (int ww = 0; ww < kNW; ++ww) any_bad = any_bad || s_bad[ww] != 0;
+  for (int ww = 0; ww < kNW; ++ww) bad_or |= s_bad[ww];
+  const bool any_bad = bad_or != 0;
   for (int idx = threadIdx.x; idx < kRowsN * kD; idx += kNW * 64) {
     const int rr = idx / kD, d = idx % kD;
     const int r = rr / GQ;
     if (r >= L) continue;
+    // no branch on the maxima: every read can go out at once (weight 0 for a
+    // wavefront with no finite score)
     float M = neg_inf();
 #pragma unroll
     for (int ww = 0; ww < kNW; ++ww) M = fmaxf(M, ml[(ww * kRowsN + rr) * 2]);
     float Lt = 0.f, O = 0.f;
-    if (M != neg_inf()) {
 #pragma unroll
-      for (int ww = 0; ww < kNW; ++ww) {
-        const float mw = ml[(ww * kRowsN + rr) * 2];
-        const float a = (mw == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-        Lt += ml[(ww * kRowsN + rr) * 2 + 1] * a;
-        O += mo[(ww * kRowsN + rr) * kD + d] * a;
-      }
+    for (int ww = 0; ww < kNW; ++ww) {
+      const float mw = ml[(ww * kRowsN + rr) * 2];
+      const float a = (mw == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      Lt += ml[(ww * kRowsN + rr) * 2 + 1] * a;
+      O += mo[(ww * kRowsN + rr) * kD + d] * a;
     }
     const size_t orow = static_cast<size_t>(q0 + r) * Hq + kh * GQ + rr % GQ;
     p.o[orow * kD + d] = any_bad ? qnan() : O * norm_inv(Lt);
