@@ -2,8 +2,9 @@
 size, cache and q dtype the library builds, random context lengths (block
 multiples and ragged tails), random split counts (past the block count too:
 empty splits), split and balanced decode modes, and random chunk / prefix
-lengths for chunked prefill, and chunks of a few rows per sequence (the
-decode-shaped paths of the chunked call). The cases are drawn once, from a
+lengths for chunked prefill, chunks of a few rows per sequence (the
+decode-shaped paths of the chunked call), and longer contexts cut into many
+splits. The cases are drawn once, from a
 fixed seed, so every run tests the same ones."""
 
 from __future__ import annotations
@@ -75,9 +76,33 @@ def _few_row_cases(n_cases: int = 12, seed: int = 20261204):
     return cases
 
 
+def _long_split_cases(n_cases: int = 8, seed: int = 20261205):
+    """Longer contexts cut into many splits: past 8 splits per sequence the
+    bf16 decode keeps two blocks in flight per wavefront and the combine runs
+    four wavefronts per pair, past 64 it takes a wavefront's splits in several
+    chunks."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n_cases):
+        D = int(rng.choice([64, 128]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        hkv = int(rng.choice([1, 2]))
+        kv = "bf16" if i % 2 == 0 else str(rng.choice(["f32", "i8", "fp8"]))
+        qd = str(rng.choice(["f32", "bf16"]))
+        B = int(rng.integers(1, 5))
+        ctx = rng.integers(700, 6001, size=B)
+        blocks = -(-ctx // 16)
+        ns = np.minimum(rng.integers(8, 161, size=B), blocks + 1).astype(np.int32)
+        cases.append(dict(id=f"l{i}_D{D}_g{g}_h{hkv}_{kv}_q{qd}_B{B}_ns{int(ns.max())}", D=D, g=g, hkv=hkv, kv=kv,
+                          qd=qd, ctx=[int(c) for c in ctx], ns=[int(x) for x in ns], mode="splits",
+                          seed=6000 + i))
+    return cases
+
+
 DECODE = _decode_cases()
 CHUNKED = _chunked_cases()
 FEW_ROWS = _few_row_cases()
+LONG_SPLITS = _long_split_cases()
 
 
 def _check(out, ref, what, case):
@@ -102,6 +127,19 @@ def test_random_decode(gpu, case):
                                                 G.ints(ctx, gpu), None, 0, float(step.scale), return_lse=True)
         torch.cuda.synchronize()
         out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    ro, rl = O.decode(step, O.pool(step))
+    _check(out, ro, "out", case)
+    _check(lse, rl, "lse", case)
+
+
+@pytest.mark.parametrize("case", LONG_SPLITS, ids=[c["id"] for c in LONG_SPLITS])
+def test_random_long_split_decode(gpu, case):
+    scaled = case["kv"] in ("i8", "fp8")
+    step = W.make_step(case["id"], case["ctx"], [1] * len(case["ctx"]), num_q_heads=case["g"] * case["hkv"],
+                       num_kv_heads=case["hkv"], head_dim=case["D"], q_dtype=case["qd"], kv_dtype=case["kv"],
+                       src_dtype=(case["qd"] if scaled else case["kv"]), num_splits=case["ns"], seed=case["seed"])
+    cache = G.build_cache(step, gpu)
+    out, lse = G.run_decode(step, cache, gpu)
     ro, rl = O.decode(step, O.pool(step))
     _check(out, ro, "out", case)
     _check(lse, rl, "lse", case)
