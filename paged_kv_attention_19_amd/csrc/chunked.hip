@@ -638,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
   // (V in stage sv_stage) || this group's half of tile j + 2 from st to
   // stage st_stage, then tile j + 3's loads (from ns) into st; 8 slots of two
   // bf16 MFMAs (8-bit caches: one fp16 MFMA) on different accumulators.
-  auto phase2 = [&](int j, int sv_stage, int st_stage, Staged& st, const TileSrc& ns) {
+  auto phase2 = [&](int sv_stage, int st_stage, Staged& st, const TileSrc& ns) {
     const int vo = sv_stage * kKBytes;   // V^T stage read
     const int wo = st_stage * kKBytes;   // stage written
     uint4 va[2][kDB];
@@ -768,7 +768,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkedParams p) {
     __builtin_amdgcn_sched_barrier(0);
     phase1(diag_tag, j, S1, S);
     __syncthreads();
-    phase2(j, S, S2, sa, ns);
+    phase2(S, S2, sa, ns);
     __syncthreads();
   };
   using I0 = std::integral_constant<int, 0>;

@@ -595,8 +595,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
 
   // block ids of the load cursor's sequence, 64 per fetch (lane j -> block c*64+j)
   int id_b = -1, id_chunk = -1, ids = 0;
-  bool bad = false;   // an id outside the pool: the current segment comes out NaN
-  bool seg_bad = false;
+  bool seg_bad = false;   // an id outside the pool: the current segment comes out NaN
   auto block_id = [&](int cb, int cblk) -> int {
     if (cb != id_b || (cblk >> 6) != id_chunk) {
       id_b = cb;
@@ -784,7 +783,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeParams p) {
   };
 
   int64_t pos = r0;
-  for (int64_t it = 0; pos < r1; it += PD + 1) {
+  while (pos < r1) {
 #pragma unroll
     for (int k = 0; k <= PD; ++k) {
       if (pos < r1) {
