@@ -5,7 +5,7 @@
  * Decode attention is bound by HBM reads: its time goes to streaming the KV
  * cache once (page "llm-inference" on shehab-ashraf.github.io, section "KV
  * Cache": decode is memory-bound; course README "Build an LLM Inference
- * Engine From Scratch", curriculum S06/S12). Its speed is best judged against
+ * Engine From Scratch", curriculum S06/S12). Its speed is best compared with
  * what a kernel that only reads the same number of bytes reaches on the same
  * machine in the same run, launch and drain included.
  */
