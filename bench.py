@@ -189,7 +189,8 @@ def copy_calibration(nbytes: int) -> None:
 
 def time_windows(fn_per_step, reps, steps, steps_per_graph, warmup, min_seconds):
     """Time windows of exactly ``steps`` consecutive steps (rotating over the
-    replicas), captured in HIP graphs of at most ``steps_per_graph`` steps, and
+    replicas), captured as one HIP graph when ``steps <= steps_per_graph``, else
+    in graphs of whole rotations of at most ``steps_per_graph`` steps, and
     replayed back to back until at least ``min_seconds`` of GPU time and
     WINDOWS_MIN windows have run. Returns (median seconds per window, windows,
     total timed seconds)."""
@@ -203,10 +204,13 @@ def time_windows(fn_per_step, reps, steps, steps_per_graph, warmup, min_seconds)
                 fn_per_step(reps[(start + i) % R])
         return g
 
-    per = max(1, min(steps_per_graph, steps))
-    per = max(R, (per // R) * R)          # whole rotations inside a graph
-    n_full = steps // per
-    rem = steps % per
+    if steps <= steps_per_graph:
+        # the whole window in one graph: one launch per window of steps
+        per, n_full, rem = steps, 1, 0
+    else:
+        per = max(R, (steps_per_graph // R) * R)   # whole rotations inside a graph replayed several times
+        n_full = steps // per
+        rem = steps % per
     g_full = capture(per, 0) if n_full else None
     g_rem = capture(rem, 0) if rem else None
 
