@@ -730,9 +730,10 @@ def main():
     kv_step, seqs_step, value = decode_figures(reps, args, per_step, steps)
 
     # per-kernel launch durations: graphs holding one kind of launch, timed
-    # in windows the same way
+    # in windows the same way, of 4096 launches whatever --steps is (so that
+    # a graph's own launch is spread over enough kernel launches)
     per_kernel = {}
-    n_k = min(steps, 4096)
+    n_k = 4096
     fused = reps[0].fused
     dom = "decode_balanced" if reps[0].balanced else ("decode_append" if fused else "decode_partial")
     sp, _, _ = time_windows(lambda r: r.partials(), reps, n_k, args.steps_per_graph, 64, args.min_seconds)
