@@ -158,7 +158,7 @@ def parse():
     ap.add_argument("--no-chunked", action="store_true", help="skip the chunked-prefill MFMA measurement")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the other decode configurations and the speculative-verify shape")
-    ap.add_argument("--chunked-kv", choices=("i8", "fp8"), default="i8",
+    ap.add_argument("--chunked-kv", choices=("i8", "fp8", "bf16"), default="i8",
                     help="KV cache dtype of the mixed step in the chunked-prefill measurement")
     ap.add_argument("--no-fuse", action="store_true",
                     help="write the new rows with a separate reshape_and_cache launch instead of inside the decode")
@@ -486,7 +486,7 @@ def timed_graph(fn, calls_per_graph, min_seconds, check=None):
 
 
 def measure_chunked(dev, min_seconds, kv_dtype: str = "i8"):
-    """The mixed int8 (or fp8) step: 4 x 512-row causal chunks over a
+    """The mixed int8 (or fp8, bf16) step: 4 x 512-row causal chunks over a
     1536-token cached prefix plus 124 decode rows. Times the chunked (MFMA)
     pass alone, and the whole step (cache write of 2172 rows, chunked pass,
     decode pass)."""
@@ -496,7 +496,8 @@ def measure_chunked(dev, min_seconds, kv_dtype: str = "i8"):
     import paged_kv_attention_19_amd as pkv
     import workloads as W
     step = W.mixed_int8(kv_dtype=kv_dtype, max_tokens_per_split=MIXED_SPLIT)
-    cache = pkv.KVCache.allocate(step.num_blocks, 8, 128, {"i8": pkv.I8, "fp8": pkv.FP8}[kv_dtype], dev)
+    cache = pkv.KVCache.allocate(step.num_blocks, 8, 128, {"i8": pkv.I8, "fp8": pkv.FP8, "bf16": pkv.BF16}[kv_dtype],
+                                 dev)
     pkv.reshape_and_cache(_dt(step.prefix_k, "bf16", dev), _dt(step.prefix_v, "bf16", dev),
                           _dt(step.prefix_slots.astype(np.int64), "i64", dev), cache)
     new_k, new_v = _dt(step.new_k, "bf16", dev), _dt(step.new_v, "bf16", dev)
@@ -528,7 +529,7 @@ def measure_chunked(dev, min_seconds, kv_dtype: str = "i8"):
     t_step, _ = timed_graph(whole, 20, min_seconds, check=lambda: (out_c.clone(), out_d.clone()))
     flops = chunked_flops(step)
     tflops = flops / t_chunked / 1e12
-    kv_name = {"i8": "int8", "fp8": "fp8"}[kv_dtype]
+    kv_name = {"i8": "int8", "fp8": "fp8", "bf16": "bf16"}[kv_dtype]
     prof = profile_figures(CHUNKED_PROFILE, CHUNKED_FILES, kv_dtype=kv_dtype)
     return {
         "workload": f"4 x 512-row causal chunks over 1536-token {kv_name} prefixes (16q/8kv/128), "
