@@ -187,6 +187,19 @@ def copy_calibration(nbytes: int) -> None:
     print(json.dumps({"copy_bytes": nbytes, "copies": 8}), flush=True)
 
 
+def window_plan(steps: int, steps_per_graph: int, replicas: int):
+    """How a window of exactly ``steps`` steps is captured: ``(per, n_full,
+    rem)`` = ``n_full`` replays of a graph of ``per`` steps, then one graph of
+    ``rem`` steps (none if 0). Up to ``steps_per_graph`` steps the window is one
+    graph; past that the repeated graph holds whole rotations over the
+    replicas, so every replay starts at replica 0 and the window's steps still
+    visit the replicas in order."""
+    if steps <= steps_per_graph:
+        return steps, 1, 0
+    per = max(replicas, (steps_per_graph // replicas) * replicas)
+    return per, steps // per, steps % per
+
+
 def time_windows(fn_per_step, reps, steps, steps_per_graph, warmup, min_seconds):
     """Time windows of exactly ``steps`` consecutive steps (rotating over the
     replicas), captured as one HIP graph when ``steps <= steps_per_graph``, else
@@ -204,13 +217,7 @@ def time_windows(fn_per_step, reps, steps, steps_per_graph, warmup, min_seconds)
                 fn_per_step(reps[(start + i) % R])
         return g
 
-    if steps <= steps_per_graph:
-        # the whole window in one graph: one launch per window of steps
-        per, n_full, rem = steps, 1, 0
-    else:
-        per = max(R, (steps_per_graph // R) * R)   # whole rotations inside a graph replayed several times
-        n_full = steps // per
-        rem = steps % per
+    per, n_full, rem = window_plan(steps, steps_per_graph, R)
     g_full = capture(per, 0) if n_full else None
     g_rem = capture(rem, 0) if rem else None
 
