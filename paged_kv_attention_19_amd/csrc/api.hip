@@ -135,19 +135,18 @@ int decode_waves(int /*max_blocks_per_seq*/, int /*max_num_splits*/) {
 // a group of num_q_heads; the kernel uses group * (head_dim + 1) floats per
 // slot.)
 // Chunks of at most this many query rows per kv head (max_q_len times the GQA
-// group) go to the decode kernels rather than the MFMA kernel: with so few
-// rows a 128-row MFMA tile is mostly empty, while the decode kernels stream
-// the K/V tiles once with every row in registers. Their VALU work grows with
-// the rows, so past 4 rows the MFMA kernel is faster. Measured on MI355X, 32
-// sequences of 128..384 tokens (bf16, 8 kv heads), L new rows each with G
-// query heads per kv head, decode kernels against MFMA kernel: L x G = 1 or
-// 2: 9.9-10.1 against 18.0-18.8 us; 4: 13.0-13.2 against 18.1-18.8 us; 8:
-// 23.8-25.0 against 18.3-19.9 us.
+// group) go to the decode kernels rather than an MFMA kernel: with so few
+// rows an MFMA tile is mostly empty, while the decode kernels stream the K/V
+// tiles once with every row in registers. Their VALU work grows with the
+// rows. Measured on MI355X, 32 sequences of 128..384 tokens (8 kv heads), L
+// new rows each with G query heads per kv head. Against the 128-row MFMA
+// kernel, the decode kernels take 9.6-10.1 us at L x G = 1 or 2 (18.0-18.8),
+// 13.0-13.2 at 4 (18.1-18.8) and 23.8-25.0 at 8 (18.3-19.9). Against the
+// few-row MFMA kernel below, with head dims of 128: 9.6 at 2 rows (L 1, G 2)
+// on either, then 12.9 against 11.8 at 3 (L 3, G 1), 12.7-13.1 against 12.0
+// at 4 (L 2, G 2; L 4, G 1) and 13.7 against 10.9 at 4 over an int8 cache.
 constexpr int kRowsDecodeMax = 4;
-// Up to 16 rows per kv head: a decode-shaped kernel on 16x16 MFMAs (one
-// workgroup per (sequence, kv head), the rows as the MFMA's N side). Same
-// workload: 15.2 us at 8 rows per kv head (L 4, G 2) and 16.6 us at 16 (L 8,
-// G 2 or L 16, G 1), against 18.9-20.2 us on the 128-row MFMA kernel.
+constexpr int kRowsDecodeMax128 = 2;
 constexpr int kRowsMfmaMax = 16;
 
 constexpr int kBalancedMaxWorkgroups = 512;
@@ -597,11 +596,13 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
   if (pkv_status st = debug_validate(fn, dr, stream); st != PKV_OK) return st;
   const int group = num_q_heads / cache->num_kv_heads;
   const int64_t rows = static_cast<int64_t>(max_q_len) * group;
-  if (rows <= kRowsDecodeMax || (rows <= kRowsMfmaMax && cache->head_dim == 128)) {
-    // chunks of a few rows (speculative verification): the decode kernels,
-    // with every chunk row of a kv head's query heads on each K/V tile (the
-    // MFMA one is built for head dims of 128; with 64, chunks of 5 to 16 rows
-    // per kv head take the chunk kernel below)
+  const bool mfma_rows = cache->head_dim == 128;
+  const int decode_max = mfma_rows ? kRowsDecodeMax128 : kRowsDecodeMax;
+  if (rows <= decode_max || (mfma_rows && rows <= kRowsMfmaMax)) {
+    // chunks of a few rows (speculative verification): the decode kernels or
+    // the few-row MFMA kernel, with every chunk row of a kv head's query
+    // heads on each K/V tile (the MFMA one is built for head dims of 128; with
+    // 64, chunks of 5 to 16 rows per kv head take the chunk kernel below)
     pkv::DecodeParams dp{};
     dp.q = q;
     dp.k = cache->k;
@@ -623,7 +624,7 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
     dp.max_q_len = max_q_len;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (rows > kRowsDecodeMax) {
+    if (rows > decode_max) {
       e = pkv::launch_rows_mfma(dp, cache->kv_dtype, cache->head_dim, group, st);
     } else {
       switch (cache->kv_dtype) {

@@ -32,6 +32,12 @@ __device__ __forceinline__ uint4 buffer_load_nt16(__amdgpu_buffer_rsrc_t r, int 
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// The same with the default cache policy.
+__device__ __forceinline__ uint4 buffer_load_plain16(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // 4-byte float load at byte offset `off` of a buffer (0 past its end).
 __device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));

@@ -1,8 +1,8 @@
 """GPU parity of the chunked entry point's paths for chunks of a few rows
 (speculative verification: k draft rows per sequence). When max_q_len times
-the GQA group is at most 4, the rows are computed by the decode kernels (up
-to 16: by a decode-shaped kernel on 16x16 MFMAs),
-every chunk row of a kv head's query heads on each K/V tile, with row r of an
+the GQA group is at most 2 (4 with head_dim 64), the rows are computed by the
+decode kernels (up to 16, with head_dim 128: by a decode-shaped kernel on
+16x16 MFMAs), every chunk row of a kv head's query heads on each K/V tile, with row r of an
 L-row chunk seeing tokens t <= n - L + r. Same tolerance as the other decode
 tests; indexing checked bit for bit with a one-hot probe."""
 
@@ -26,16 +26,16 @@ def check(got, ref, what):
 
 @pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
 @pytest.mark.parametrize("Hq,Hkv,ql", [
-    (16, 8, [2, 1, 2, 2, 1, 2]),       # group 2: up to 2 rows (4 rows per kv head)
-    (8, 8, [4, 3, 1, 4, 4, 2]),        # group 1: up to 4 rows
-    (16, 4, [1, 1, 1, 1, 1, 1]),       # group 4: one row per sequence through the chunked call
-    (16, 8, [1, 1, 1, 1, 1, 1]),       # group 2: one row (2 rows per kv head)
+    (8, 8, [2, 1, 2, 2, 1, 2]),        # group 1: up to 2 rows
+    (8, 4, [1, 1, 1, 1, 1, 1]),        # group 2: one row per sequence through the chunked call
+    (16, 16, [1, 1, 1, 1, 1, 1]),      # group 1: one row
 ])
 def test_few_row_chunks_match_oracle(gpu, kv, Hq, Hkv, ql):
+    """head_dim 128, up to 2 rows per kv head: the decode kernels."""
     ctx = [300, 77, 1025, 8, 129, 2000]
     step = W.make_step(f"rows_{kv}_{Hq}_{Hkv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,
                        kv_dtype=kv, src_dtype="bf16", seed=600 + Hkv + max(ql))
-    assert max(ql) * (Hq // Hkv) <= 4
+    assert max(ql) * (Hq // Hkv) <= 2
     cache = G.build_cache(step, gpu)
     # every sequence's rows as one chunk each (one-row chunks included)
     q, cu, tables, ctx = step.q, step.cu_q_lens, step.block_tables, step.context_lens
@@ -92,11 +92,12 @@ def test_spec_verify_shape_matches_oracle(gpu):
 
 @pytest.mark.parametrize("kv", ["bf16", "i8"])
 def test_few_row_one_hot_rows_before_and_after_the_hot_key(gpu, kv):
-    """2 rows per sequence at positions n-2, n-1 (4 rows per kv head: the
-    decode kernels); key 0 is warm, key n-1 is hot, every other key zero: row
-    n-2 returns V_0 and row n-1 returns V_{n-1}, bit for bit."""
+    """2 rows per sequence at positions n-2, n-1 (one query head per kv head,
+    2 rows per kv head: the decode kernels); key 0 is warm, key n-1 is hot,
+    every other key zero: row n-2 returns V_0 and row n-1 returns V_{n-1}, bit
+    for bit."""
     import torch
-    Hq, Hkv, D = 16, 8, 128
+    Hq, Hkv, D = 8, 8, 128
     ctx = [300, 45, 17]
     ql = [2, 2, 2]
     step = W.make_step(f"rows1hot_{kv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, kv_dtype=kv,
@@ -130,15 +131,15 @@ def test_few_row_one_hot_rows_before_and_after_the_hot_key(gpu, kv):
         for r in range(2):
             src = n - 1 if n - 2 + r >= n - 1 else 0
             for h in range(Hq):
-                assert np.array_equal(out[cu[i] + r, h], V[src, h // 2].astype(np.float32)), (kv, i, r, h)
+                assert np.array_equal(out[cu[i] + r, h], V[src, h].astype(np.float32)), (kv, i, r, h)
 
 
 def test_few_row_path_agrees_with_the_mfma_path(gpu):
-    """The same 2-row chunks through the few-row path (16 q / 8 kv heads,
-    4 rows per kv head) and, with a larger max_q_len, through the MFMA
+    """The same 2-row chunks through the decode kernels (8 q / 8 kv heads,
+    2 rows per kv head) and, with a larger max_q_len, through the 128-row MFMA
     kernel: both within tolerance of the oracle and of each other."""
     import torch
-    step = W.make_step("rows_vs_mfma", [300, 77, 1025], [2, 2, 2], num_q_heads=16, num_kv_heads=8, head_dim=128,
+    step = W.make_step("rows_vs_mfma", [300, 77, 1025], [2, 2, 2], num_q_heads=8, num_kv_heads=8, head_dim=128,
                        seed=612)
     cache = G.build_cache(step, gpu)
     q, cu, tables, ctx = step.chunk_batch()
@@ -157,10 +158,10 @@ def test_few_row_path_agrees_with_the_mfma_path(gpu):
 def test_few_row_bad_metadata_and_empty_chunks(gpu):
     """A chunk longer than its context or than max_q_len comes out NaN, an
     out-of-pool block id poisons its sequence, a zero-row chunk writes
-    nothing, and the other sequences are unaffected (2-row chunks, 4 rows per
+    nothing, and the other sequences are unaffected (2-row chunks, 2 rows per
     kv head: the decode kernels)."""
     import torch
-    step = W.make_step("rows_bad", [100, 100, 100, 100], [2, 2, 2, 2], num_q_heads=16, num_kv_heads=8,
+    step = W.make_step("rows_bad", [100, 100, 100, 100], [2, 2, 2, 2], num_q_heads=8, num_kv_heads=8,
                        head_dim=128, seed=613)
     cache = G.build_cache(step, gpu)
     ro, _ = O.chunked(step, O.pool(step))
@@ -172,7 +173,7 @@ def test_few_row_bad_metadata_and_empty_chunks(gpu):
     cu2 = cu.copy()
     cu2[3] = cu2[2]                    # sequence 2 has an empty chunk; sequence 3 takes 4 rows
     G.announce("few-row bad metadata")
-    out = torch.full((len(q), 16, 128), 7.0, dtype=torch.float32, device=gpu)
+    out = torch.full((len(q), 8, 128), 7.0, dtype=torch.float32, device=gpu)
     G.pkv.paged_attention_chunked(G.tensor(q, "bf16", gpu), G.ints(cu2, gpu), 2, cache, G.ints(tables, gpu),
                                   G.ints(ctx, gpu), float(step.scale), out=out)
     torch.cuda.synchronize()
@@ -189,7 +190,7 @@ def test_few_row_bad_metadata_and_empty_chunks(gpu):
 
 
 # ---------------------------------------------------------------------------
-# 5 .. 16 rows per kv head: the decode-shaped MFMA kernel
+# 3 .. 16 rows per kv head: the decode-shaped MFMA kernel
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
@@ -199,6 +200,10 @@ def test_few_row_bad_metadata_and_empty_chunks(gpu):
     (8, 8, [16, 9, 1, 16, 7, 12]),     # group 1: up to 16 rows
     (16, 4, [4, 1, 3, 4, 2, 4]),       # group 4: up to 4 rows
     (16, 2, [2, 1, 2, 2, 1, 2]),       # group 8: up to 2 rows
+    (16, 8, [2, 1, 2, 2, 1, 2]),       # group 2: up to 2 rows (4 rows per kv head)
+    (8, 8, [4, 3, 1, 4, 4, 2]),        # group 1: up to 4 rows
+    (8, 8, [3, 1, 3, 2, 3, 3]),        # group 1: up to 3 rows
+    (16, 4, [1, 1, 1, 1, 1, 1]),       # group 4: one row per sequence
 ])
 def test_mfma_few_row_chunks_match_oracle(gpu, kv, Hq, Hkv, ql):
     """Contexts from 16 tokens to 5,000 (more than 64 blocks per wavefront,
@@ -207,7 +212,7 @@ def test_mfma_few_row_chunks_match_oracle(gpu, kv, Hq, Hkv, ql):
     ctx = [300, 77, 5000, 16, 129, 2000]
     step = W.make_step(f"mrows_{kv}_{Hq}_{Hkv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,
                        kv_dtype=kv, src_dtype="bf16", seed=700 + Hkv + max(ql))
-    assert 4 < max(ql) * (Hq // Hkv) <= 16
+    assert 2 < max(ql) * (Hq // Hkv) <= 16
     cache = G.build_cache(step, gpu)
     q, cu, tables, ctx_ = step.q, step.cu_q_lens, step.block_tables, step.context_lens
     G.announce(f"MFMA few-row chunks {step.name} max_q_len={max(ql)}")

@@ -58,8 +58,9 @@ def _chunked_cases(n_cases: int = 16, seed: int = 20261203):
 
 def _few_row_cases(n_cases: int = 12, seed: int = 20261204):
     """Chunks of 1 to 16 / G rows per sequence, one-row chunks among them, over
-    random prefixes: up to 4 rows per kv head take the decode kernels, 5 to 16
-    the 16x16 MFMA kernel."""
+    random prefixes: up to 2 rows per kv head (4 with head_dim 64) take the
+    decode kernels, more up to 16 the 16x16 MFMA kernel (the chunk kernel with
+    head_dim 64)."""
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n_cases):
