@@ -285,8 +285,9 @@ pkv_status pkv_paged_attention_decode_append(const void* k_new, const void* v_ne
  * (sequence, kv head)
  * streaming the sequence once with every chunk row of the group's query heads
  * against each K/V tile:
- *   R <= 4      : fp32 FMAs and dot products (the decode's arithmetic);
- *   4 < R <= 16 : (head_dim 128) 16x16 bf16 MFMAs for QK^T and PV, the weights split into a
+ *   R <= 2 (head_dim 128), R <= 4 (head_dim 64):
+ *                 fp32 FMAs and dot products (the decode's arithmetic);
+ *   2 < R <= 16 : (head_dim 128) 16x16 bf16 MFMAs for QK^T and PV, the weights split into a
  *                 bf16 high part and residual (~2^-17), 8-bit codes converted
  *                 to bf16 exactly;
  * e.g. speculative verification of up to 8 draft rows with 2 query heads per

@@ -142,9 +142,11 @@ int decode_waves(int /*max_blocks_per_seq*/, int /*max_num_splits*/) {
 // new rows each with G query heads per kv head. Against the 128-row MFMA
 // kernel, the decode kernels take 9.6-10.1 us at L x G = 1 or 2 (18.0-18.8),
 // 13.0-13.2 at 4 (18.1-18.8) and 23.8-25.0 at 8 (18.3-19.9). Against the
-// few-row MFMA kernel below, with head dims of 128: 9.6 at 2 rows (L 1, G 2)
-// on either, then 12.9 against 11.8 at 3 (L 3, G 1), 12.7-13.1 against 12.0
-// at 4 (L 2, G 2; L 4, G 1) and 13.7 against 10.9 at 4 over an int8 cache.
+// few-row MFMA kernel below, with head dims of 128: 8.4-9.8 against
+// 10.0-11.6 at 2 rows (L 1, G 2 or L 2, G 1; bf16, int8 and fp8 caches);
+// then the MFMA kernel leads, 12.9 against 11.8 at 3 rows (L 3, G 1), at 4
+// 12.3-13.1 against 12.0 over bf16, 13.4-14.0 against 10.8-10.9 over int8
+// and 12.7-13.3 against 10.4 over fp8.
 constexpr int kRowsDecodeMax = 4;
 constexpr int kRowsDecodeMax128 = 2;
 constexpr int kRowsMfmaMax = 16;
