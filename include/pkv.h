@@ -309,6 +309,23 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
                                        float* out_lse, void* stream);
 
 /*
+ * chunked_kernel_for: which kernel pkv_paged_attention_chunked runs for a call
+ * of this shape, by the rule above (host only: no GPU, no allocation):
+ *   PKV_CHUNKED_DECODE_ROWS : the decode core, R <= 2 (head_dim 128) or
+ *                             R <= 4 (head_dim 64);
+ *   PKV_CHUNKED_ROWS_MFMA   : the 16x16 MFMA few-row kernel, 2 < R <= 16
+ *                             (head_dim 128);
+ *   PKV_CHUNKED_TILES       : the 128-row MFMA kernel, every longer chunk.
+ * R = max_q_len * (num_q_heads / num_kv_heads). Returns -1 (and sets
+ * pkv_last_error) for a shape the entry point rejects: max_q_len < 1,
+ * num_kv_heads < 1, a GQA group outside {1, 2, 4, 8}, head_dim not 64 or 128.
+ */
+#define PKV_CHUNKED_DECODE_ROWS 1
+#define PKV_CHUNKED_ROWS_MFMA 2
+#define PKV_CHUNKED_TILES 3
+int32_t pkv_chunked_kernel_for(int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim);
+
+/*
  * lse_combine: merge split partials (each normalised by its own denominator)
  * by log-sum-exp: M = max_s lse_s over splits with lse_s > -inf,
  * w_s = exp(lse_s - M), out = sum_s w_s o_s / sum_s w_s, lse = M + log sum_s w_s.

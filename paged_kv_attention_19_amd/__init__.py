@@ -26,11 +26,14 @@ __all__ = [
     "F32", "BF16", "I8", "FP8", "PkvError", "KVCache", "lib", "library_path", "exported_symbols",
     "reshape_and_cache", "decode_workspace_bytes", "decode_default_max_num_splits", "paged_attention_decode",
     "paged_attention_decode_append", "paged_attention_decode_noalloc", "paged_attention_chunked", "lse_combine",
-    "version", "NOALLOC_SCRATCH_BYTES", "stream_read",
+    "version", "NOALLOC_SCRATCH_BYTES", "stream_read", "chunked_kernel_for", "CHUNKED_DECODE_ROWS",
+    "CHUNKED_ROWS_MFMA", "CHUNKED_TILES",
 ]
 
 F32, BF16, I8, FP8 = 0, 1, 2, 3
 NOALLOC_SCRATCH_BYTES = 48 << 20   # PKV_NOALLOC_SCRATCH_BYTES of the C header
+# kernels of the chunked entry point (PKV_CHUNKED_* of the C header)
+CHUNKED_DECODE_ROWS, CHUNKED_ROWS_MFMA, CHUNKED_TILES = 1, 2, 3
 _TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8, FP8: torch.float8_e4m3fn}
 _CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.float8_e4m3fn: FP8}
 _SCALED = (I8, FP8)   # 8-bit codes with a float32 scale per (token, kv head)
@@ -72,6 +75,7 @@ _SIGS = {
     "pkv_reshape_and_cache": ([_P, _P, _I32, _P, _I32, ctypes.POINTER(_Cache), _P], _I32),
     "pkv_decode_workspace_bytes": ([_I32, _I32, _I32, _I32], ctypes.c_size_t),
     "pkv_decode_default_max_num_splits": ([_I32], _I32),
+    "pkv_chunked_kernel_for": ([_I32, _I32, _I32, _I32], _I32),
     "pkv_paged_attention_decode": ([_P, _I32, _I32, _I32, ctypes.POINTER(_Cache), _P, _I32, _P, _P, _I32,
                                     ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], _I32),
     "pkv_paged_attention_decode_append": ([_P, _P, _I32, _P, _P, _I32, _I32, _I32, ctypes.POINTER(_Cache), _P, _I32,
@@ -284,6 +288,15 @@ def decode_default_max_num_splits(max_blocks_per_seq: int) -> int:
     """The library's choice of decode mode for a table width, for calls
     without a split plan: 1 (one split per sequence) or 0 (balanced)."""
     r = int(lib().pkv_decode_default_max_num_splits(max_blocks_per_seq))
+    if r < 0:
+        raise PkvError(-1, lib().pkv_last_error().decode())
+    return r
+
+
+def chunked_kernel_for(max_q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
+    """The kernel ``paged_attention_chunked`` runs for this call shape (host
+    only): CHUNKED_DECODE_ROWS, CHUNKED_ROWS_MFMA or CHUNKED_TILES."""
+    r = int(lib().pkv_chunked_kernel_for(max_q_len, num_q_heads, num_kv_heads, head_dim))
     if r < 0:
         raise PkvError(-1, lib().pkv_last_error().decode())
     return r

@@ -151,6 +151,14 @@ constexpr int kRowsDecodeMax = 4;
 constexpr int kRowsDecodeMax128 = 2;
 constexpr int kRowsMfmaMax = 16;
 
+// The chunked entry point's kernel for R = max_q_len * group rows per kv head.
+int chunked_kernel_of(int64_t rows, int head_dim) {
+  const bool mfma_rows = head_dim == 128;   // the few-row MFMA kernel is built for 128
+  if (rows <= (mfma_rows ? kRowsDecodeMax128 : kRowsDecodeMax)) return PKV_CHUNKED_DECODE_ROWS;
+  if (mfma_rows && rows <= kRowsMfmaMax) return PKV_CHUNKED_ROWS_MFMA;
+  return PKV_CHUNKED_TILES;
+}
+
 constexpr int kBalancedMaxWorkgroups = 512;
 size_t balanced_part_bytes(int heads_per_slot, int head_dim) {
   return static_cast<size_t>(kBalancedMaxWorkgroups) * 4 * 2 * heads_per_slot * (head_dim + 1) * sizeof(float);
@@ -550,6 +558,20 @@ pkv_status pkv_lse_combine(const float* o_part, const float* lse_part, int32_t b
   return ok();
 }
 
+int32_t pkv_chunked_kernel_for(int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  const char* fn = "pkv_chunked_kernel_for";
+  if (max_q_len < 1 || num_kv_heads < 1) {
+    fail(PKV_ERR_INVALID_ARG, "%s: max_q_len=%d, num_kv_heads=%d", fn, max_q_len, num_kv_heads);
+    return -1;
+  }
+  if (check_group(num_q_heads, num_kv_heads, fn) != PKV_OK) return -1;
+  if (head_dim != 64 && head_dim != 128) {
+    fail(PKV_ERR_UNSUPPORTED, "%s: head_dim=%d (built: 64, 128)", fn, head_dim);
+    return -1;
+  }
+  return chunked_kernel_of(static_cast<int64_t>(max_q_len) * (num_q_heads / num_kv_heads), head_dim);
+}
+
 pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
                                        const int32_t* cu_q_lens, int32_t max_q_len, const pkv_cache* cache,
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -598,9 +620,8 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
   if (pkv_status st = debug_validate(fn, dr, stream); st != PKV_OK) return st;
   const int group = num_q_heads / cache->num_kv_heads;
   const int64_t rows = static_cast<int64_t>(max_q_len) * group;
-  const bool mfma_rows = cache->head_dim == 128;
-  const int decode_max = mfma_rows ? kRowsDecodeMax128 : kRowsDecodeMax;
-  if (rows <= decode_max || (mfma_rows && rows <= kRowsMfmaMax)) {
+  const int path = chunked_kernel_of(rows, cache->head_dim);
+  if (path != PKV_CHUNKED_TILES) {
     // chunks of a few rows (speculative verification): the decode kernels or
     // the few-row MFMA kernel, with every chunk row of a kv head's query
     // heads on each K/V tile (the MFMA one is built for head dims of 128; with
@@ -626,7 +647,7 @@ pkv_status pkv_paged_attention_chunked(const void* q, int32_t q_dtype, int32_t n
     dp.max_q_len = max_q_len;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (rows > decode_max) {
+    if (path == PKV_CHUNKED_ROWS_MFMA) {
       e = pkv::launch_rows_mfma(dp, cache->kv_dtype, cache->head_dim, group, st);
     } else {
       switch (cache->kv_dtype) {

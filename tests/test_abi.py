@@ -27,7 +27,7 @@ def test_library_exports_every_header_function():
     names = pkv.exported_symbols()
     assert {"pkv_reshape_and_cache", "pkv_paged_attention_decode", "pkv_paged_attention_decode_append",
             "pkv_paged_attention_chunked", "pkv_lse_combine", "pkv_decode_workspace_bytes", "pkv_last_error",
-            "pkv_version", "pkv_decode_default_max_num_splits"} <= set(names)
+            "pkv_version", "pkv_decode_default_max_num_splits", "pkv_chunked_kernel_for"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert "gfx950" in pkv.version()
@@ -39,6 +39,28 @@ def test_default_decode_mode_by_table_width():
     assert [pkv.decode_default_max_num_splits(w) for w in (1, 24, 64, 65, 512, 2048)] == [1, 1, 1, 0, 0, 0]
     with pytest.raises(pkv.PkvError, match="max_blocks_per_seq=0"):
         pkv.decode_default_max_num_splits(0)
+
+
+def test_chunked_kernel_by_rows_per_kv_head():
+    """R = max_q_len x GQA group rows per kv head: the decode core up to 2
+    (head_dim 128) or 4 (head_dim 64), the 16x16 MFMA kernel up to 16 (head_dim
+    128 only), the 128-row kernel past that; rejected shapes are errors."""
+    D_ROWS, M_ROWS, TILES = pkv.CHUNKED_DECODE_ROWS, pkv.CHUNKED_ROWS_MFMA, pkv.CHUNKED_TILES
+
+    def path(L, hq, hkv, d):
+        return pkv.chunked_kernel_for(L, hq, hkv, d)
+
+    assert [path(L, 8, 8, 128) for L in (1, 2, 3, 4, 16, 17, 512)] == [D_ROWS, D_ROWS] + [M_ROWS] * 3 + [TILES] * 2
+    assert [path(L, 16, 8, 128) for L in (1, 2, 8, 9)] == [D_ROWS, M_ROWS, M_ROWS, TILES]
+    assert [path(1, 8 * g, 8, 128) for g in (1, 2, 4, 8)] == [D_ROWS, D_ROWS, M_ROWS, M_ROWS]
+    assert [path(2, 16, 2, 128), path(3, 16, 2, 128)] == [M_ROWS, TILES]      # group 8: 16 and 24 rows
+    assert [path(L, 8, 8, 64) for L in (1, 2, 3, 4, 5, 16, 17)] == [D_ROWS] * 4 + [TILES] * 3
+    assert [path(1, 8 * g, 8, 64) for g in (1, 2, 4, 8)] == [D_ROWS, D_ROWS, D_ROWS, TILES]
+    for args, msg in [((0, 8, 8, 128), "max_q_len=0"), ((1, 8, 0, 128), "num_kv_heads=0"),
+                      ((1, 12, 8, 128), "not a multiple"), ((1, 48, 3, 128), "group size 16"),
+                      ((1, 8, 8, 96), "head_dim=96")]:
+        with pytest.raises(pkv.PkvError, match=msg):
+            path(*args)
 
 
 def test_workspace_bytes():

@@ -35,7 +35,7 @@ def test_few_row_chunks_match_oracle(gpu, kv, Hq, Hkv, ql):
     ctx = [300, 77, 1025, 8, 129, 2000]
     step = W.make_step(f"rows_{kv}_{Hq}_{Hkv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,
                        kv_dtype=kv, src_dtype="bf16", seed=600 + Hkv + max(ql))
-    assert max(ql) * (Hq // Hkv) <= 2
+    assert G.pkv.chunked_kernel_for(max(ql), Hq, Hkv, 128) == G.pkv.CHUNKED_DECODE_ROWS
     cache = G.build_cache(step, gpu)
     # every sequence's rows as one chunk each (one-row chunks included)
     q, cu, tables, ctx = step.q, step.cu_q_lens, step.block_tables, step.context_lens
@@ -64,6 +64,9 @@ def test_few_row_chunks_head_dim_64(gpu, kv, Hq, Hkv, ql):
     ctx = [300, 77, 1025, 8, 129, 2000]
     step = W.make_step(f"rows64_{kv}_{Hq}_{Hkv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=64,
                        kv_dtype=kv, src_dtype="bf16", seed=640 + Hkv + max(ql))
+    rows = max(ql) * (Hq // Hkv)
+    assert G.pkv.chunked_kernel_for(max(ql), Hq, Hkv, 64) == (
+        G.pkv.CHUNKED_DECODE_ROWS if rows <= 4 else G.pkv.CHUNKED_TILES)
     cache = G.build_cache(step, gpu)
     q, cu, tables, cc = step.q, step.cu_q_lens, step.block_tables, step.context_lens
     G.announce(f"few-row chunks head_dim 64 {step.name}")
@@ -83,6 +86,7 @@ def test_spec_verify_shape_matches_oracle(gpu):
     ctx = rng.integers(128, 384, size=32, endpoint=True)
     step = W.make_step("spec_verify", ctx, np.full(32, 4), num_q_heads=16, num_kv_heads=8, head_dim=128,
                        num_blocks=4096, seed=1906)
+    assert G.pkv.chunked_kernel_for(4, 16, 8, 128) == G.pkv.CHUNKED_ROWS_MFMA
     cache = G.build_cache(step, gpu)
     out, lse = G.run_chunked(step, cache, gpu)
     ro, rl = O.chunked(step, O.pool(step))
@@ -100,6 +104,7 @@ def test_few_row_one_hot_rows_before_and_after_the_hot_key(gpu, kv):
     Hq, Hkv, D = 8, 8, 128
     ctx = [300, 45, 17]
     ql = [2, 2, 2]
+    assert G.pkv.chunked_kernel_for(2, Hq, Hkv, D) == G.pkv.CHUNKED_DECODE_ROWS
     step = W.make_step(f"rows1hot_{kv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, kv_dtype=kv,
                        src_dtype="bf16", seed=610)
     rng = np.random.default_rng(611)
@@ -212,7 +217,7 @@ def test_mfma_few_row_chunks_match_oracle(gpu, kv, Hq, Hkv, ql):
     ctx = [300, 77, 5000, 16, 129, 2000]
     step = W.make_step(f"mrows_{kv}_{Hq}_{Hkv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,
                        kv_dtype=kv, src_dtype="bf16", seed=700 + Hkv + max(ql))
-    assert 2 < max(ql) * (Hq // Hkv) <= 16
+    assert G.pkv.chunked_kernel_for(max(ql), Hq, Hkv, 128) == G.pkv.CHUNKED_ROWS_MFMA
     cache = G.build_cache(step, gpu)
     q, cu, tables, ctx_ = step.q, step.cu_q_lens, step.block_tables, step.context_lens
     G.announce(f"MFMA few-row chunks {step.name} max_q_len={max(ql)}")
@@ -243,6 +248,7 @@ def test_mfma_few_row_one_hot(gpu, kv):
     Hq, Hkv, D = 16, 8, 128
     ctx = [300, 45, 17, 1100]
     ql = [4, 4, 4, 4]
+    assert G.pkv.chunked_kernel_for(4, Hq, Hkv, D) == G.pkv.CHUNKED_ROWS_MFMA
     step = W.make_step(f"mrows1hot_{kv}", ctx, ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, kv_dtype=kv,
                        src_dtype="bf16", seed=710)
     rng = np.random.default_rng(711)

@@ -56,22 +56,25 @@ def _chunked_cases(n_cases: int = 16, seed: int = 20261203):
     return cases
 
 
-def _few_row_cases(n_cases: int = 12, seed: int = 20261204):
+def _few_row_cases(n_cases: int = 12, n_short: int = 4, seed: int = 20261204):
     """Chunks of 1 to 16 / G rows per sequence, one-row chunks among them, over
     random prefixes: up to 2 rows per kv head (4 with head_dim 64) take the
     decode kernels, more up to 16 the 16x16 MFMA kernel (the chunk kernel with
-    head_dim 64)."""
+    head_dim 64). The last ``n_short`` cases keep head_dim 128 chunks to at
+    most 2 rows per kv head, so that the decode kernels' share of the random
+    cases does not hang on the draws."""
     rng = np.random.default_rng(seed)
     cases = []
-    for i in range(n_cases):
-        g = int(rng.choice([1, 2, 4, 8]))
+    for i in range(n_cases + n_short):
+        short = i >= n_cases
+        g = int(rng.choice([1, 2] if short else [1, 2, 4, 8]))
         hkv = int(rng.choice([1, 2, 4]))
         kv = str(rng.choice(["bf16", "i8", "fp8"]))
         S = int(rng.integers(1, 25))
-        lmax = int(rng.integers(1, 16 // g + 1))
+        lmax = 2 // g if short else int(rng.integers(1, 16 // g + 1))
         L = rng.integers(1, lmax + 1, size=S)
         prefix = rng.integers(0, 900, size=S)
-        D = 64 if i % 3 == 2 else 128                    # every third case over a head_dim 64 cache
+        D = 64 if i % 3 == 2 and not short else 128     # every third case over a head_dim 64 cache
         cases.append(dict(id=f"r{i}_D{D}_g{g}_h{hkv}_{kv}_S{S}_L{int(L.max())}", D=D, g=g, hkv=hkv, kv=kv,
                           ctx=[int(a + b) for a, b in zip(prefix, L)], ql=[int(x) for x in L], seed=5000 + i))
     return cases
