@@ -459,82 +459,83 @@ def _dt(a, kind, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def timed_graph(fn, calls_per_graph, min_seconds, check=None):
-    """Median seconds per call of ``fn`` replayed from a graph of
-    ``calls_per_graph`` calls, in windows of one replay, until min_seconds."""
-    import torch
-    fn()
-    torch.cuda.synchronize()
-    ref = check() if check else None
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(calls_per_graph):
-            fn()
-    g.replay()
-    torch.cuda.synchronize()
-    if check is not None and not all(torch.equal(a, b) for a, b in zip(check(), ref)):
-        raise RuntimeError("the graph replay differs from the eager call")
-    g.replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    nwin = max(WINDOWS_MIN, math.ceil(min_seconds / max(a.elapsed_time(b) / 1e3, 1e-7)))
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nwin + 1)]
-    ev[0].record()
-    for i in range(nwin):
-        g.replay()
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    secs = sorted(ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(nwin))
-    return secs[nwin // 2] / calls_per_graph, nwin
+# Replicas of the mixed step for the chunked measurement: separate caches and
+# queries (about 600 MB each, 4.8 GB in all), the calls rotating over them, so
+# that no call finds its bytes in the caches from the one before (measured on
+# MI355X: 55.6 us per chunked call over 8 replicas against 54.2 us over one).
+CHUNKED_REPLICAS = 8
 
 
-def measure_chunked(dev, min_seconds, kv_dtype: str = "i8"):
+def measure_chunked(dev, min_seconds, kv_dtype: str = "i8", replicas: int = CHUNKED_REPLICAS):
     """The mixed int8 (or fp8, bf16) step: 4 x 512-row causal chunks over a
     1536-token cached prefix plus 124 decode rows. Times the chunked (MFMA)
     pass alone, and the whole step (cache write of 2172 rows, chunked pass,
-    decode pass)."""
+    decode pass), each rotating over ``replicas`` copies of the step (the same
+    shapes and tables, other values)."""
+    import types
+
     import numpy as np
     import torch
 
     import paged_kv_attention_19_amd as pkv
     import workloads as W
-    step = W.mixed_int8(kv_dtype=kv_dtype, max_tokens_per_split=MIXED_SPLIT)
-    cache = pkv.KVCache.allocate(step.num_blocks, 8, 128, {"i8": pkv.I8, "fp8": pkv.FP8, "bf16": pkv.BF16}[kv_dtype],
-                                 dev)
-    pkv.reshape_and_cache(_dt(step.prefix_k, "bf16", dev), _dt(step.prefix_v, "bf16", dev),
-                          _dt(step.prefix_slots.astype(np.int64), "i64", dev), cache)
-    new_k, new_v = _dt(step.new_k, "bf16", dev), _dt(step.new_v, "bf16", dev)
-    new_s = _dt(step.new_slots.astype(np.int64), "i64", dev)
-    # the step's new rows (the chunks' own K/V and the decode tokens) are in the
-    # cache before any pass reads it; the whole-step timing writes them again
-    # (the same bytes)
-    pkv.reshape_and_cache(new_k, new_v, new_s, cache)
-    qc_h, cu_h, tc_h, cc_h = step.chunk_batch()
-    qc, cu, tc, cc = _dt(qc_h, "bf16", dev), _dt(cu_h, "i32", dev), _dt(tc_h, "i32", dev), _dt(cc_h, "i32", dev)
-    max_q = int(np.diff(cu_h).max())
-    qd, td, ctxd, nsd = step.decode_batch()
-    max_ns = int(nsd.max())   # the decode rows: ceil(n / MIXED_SPLIT) splits each
-    qd, td, ctxd, nsd = _dt(qd, "bf16", dev), _dt(td, "i32", dev), _dt(ctxd, "i32", dev), _dt(nsd, "i32", dev)
-    out_c = torch.empty((qc.shape[0], 16, 128), dtype=torch.float32, device=dev)
-    out_d = torch.empty((qd.shape[0], 16, 128), dtype=torch.float32, device=dev)
-    ws = torch.zeros(max(256, pkv.decode_workspace_bytes(qd.shape[0], 16, 128, max_ns)), dtype=torch.uint8, device=dev)
-    scale = float(step.scale)
+    reps = []
+    for r in range(replicas):
+        step = W.mixed_int8(kv_dtype=kv_dtype, max_tokens_per_split=MIXED_SPLIT, values_seed=1905 + 1000 * r)
+        code = {"i8": pkv.I8, "fp8": pkv.FP8, "bf16": pkv.BF16}[kv_dtype]
+        x = types.SimpleNamespace()
+        x.cache = pkv.KVCache.allocate(step.num_blocks, 8, 128, code, dev)
+        pkv.reshape_and_cache(_dt(step.prefix_k, "bf16", dev), _dt(step.prefix_v, "bf16", dev),
+                              _dt(step.prefix_slots.astype(np.int64), "i64", dev), x.cache)
+        x.new_k, x.new_v = _dt(step.new_k, "bf16", dev), _dt(step.new_v, "bf16", dev)
+        x.new_s = _dt(step.new_slots.astype(np.int64), "i64", dev)
+        # the step's new rows (the chunks' own K/V and the decode tokens) are
+        # in the cache before any pass reads it; the whole-step timing writes
+        # them again (the same bytes)
+        pkv.reshape_and_cache(x.new_k, x.new_v, x.new_s, x.cache)
+        qc_h, cu_h, tc_h, cc_h = step.chunk_batch()
+        x.qc, x.cu, x.tc, x.cc = _dt(qc_h, "bf16", dev), _dt(cu_h, "i32", dev), _dt(tc_h, "i32", dev), _dt(cc_h, "i32", dev)
+        x.max_q = int(np.diff(cu_h).max())
+        qd, td, ctxd, nsd = step.decode_batch()
+        x.max_ns = int(nsd.max())   # the decode rows: ceil(n / MIXED_SPLIT) splits each
+        x.qd, x.td, x.ctxd, x.nsd = _dt(qd, "bf16", dev), _dt(td, "i32", dev), _dt(ctxd, "i32", dev), _dt(nsd, "i32", dev)
+        x.out_c = torch.empty((x.qc.shape[0], 16, 128), dtype=torch.float32, device=dev)
+        x.out_d = torch.empty((x.qd.shape[0], 16, 128), dtype=torch.float32, device=dev)
+        x.ws = torch.zeros(max(256, pkv.decode_workspace_bytes(x.qd.shape[0], 16, 128, x.max_ns)), dtype=torch.uint8,
+                           device=dev)
+        x.scale = float(step.scale)
+        reps.append(x)
 
-    def chunked():
-        pkv.paged_attention_chunked(qc, cu, max_q, cache, tc, cc, scale, out=out_c)
+    def chunked(x):
+        pkv.paged_attention_chunked(x.qc, x.cu, x.max_q, x.cache, x.tc, x.cc, x.scale, out=x.out_c)
 
-    def whole():
-        pkv.reshape_and_cache(new_k, new_v, new_s, cache)
-        chunked()
-        pkv.paged_attention_decode(qd, cache, td, ctxd, nsd, max_ns, scale, out=out_d, workspace=ws)
+    def whole(x):
+        pkv.reshape_and_cache(x.new_k, x.new_v, x.new_s, x.cache)
+        chunked(x)
+        pkv.paged_attention_decode(x.qd, x.cache, x.td, x.ctxd, x.nsd, x.max_ns, x.scale, out=x.out_d, workspace=x.ws)
 
-    t_chunked, nwin = timed_graph(chunked, 20, min_seconds, check=lambda: (out_c.clone(),))
-    t_step, _ = timed_graph(whole, 20, min_seconds, check=lambda: (out_c.clone(), out_d.clone()))
-    flops = chunked_flops(step)
+    def check(fn, outs):
+        """An eager call per replica, then graph replays of the same calls: the
+        outputs must agree bit for bit."""
+        for x in reps:
+            fn(x)
+        torch.cuda.synchronize()
+        eager = [[o.clone() for o in outs(x)] for x in reps]
+        for x in reps:
+            for o in outs(x):
+                o.fill_(float("nan"))
+        time_windows(fn, reps, len(reps), len(reps), 0, 0.0)
+        for x, e in zip(reps, eager):
+            if not all(torch.equal(o, eo) for o, eo in zip(outs(x), e)):
+                raise RuntimeError("the graph replay differs from the eager call")
+
+    calls = 4 * replicas   # calls per timed window
+    check(chunked, lambda x: (x.out_c,))
+    s_chunked, nwin, _ = time_windows(chunked, reps, calls, calls, calls, min_seconds)
+    check(whole, lambda x: (x.out_c, x.out_d))
+    s_step, _, _ = time_windows(whole, reps, calls, calls, calls, min_seconds)
+    t_chunked, t_step = s_chunked / calls, s_step / calls
+    flops = chunked_flops(step)   # every replica has the same shapes
     tflops = flops / t_chunked / 1e12
     kv_name = {"i8": "int8", "fp8": "fp8", "bf16": "bf16"}[kv_dtype]
     prof = profile_figures(CHUNKED_PROFILE, CHUNKED_FILES, kv_dtype=kv_dtype)
@@ -548,6 +549,7 @@ def measure_chunked(dev, min_seconds, kv_dtype: str = "i8"):
         "mfma_util": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
         "whole_step_us": round(t_step * 1e6, 3),
         "windows": nwin,
+        "replicas": replicas,
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),

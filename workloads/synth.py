@@ -267,13 +267,14 @@ def long_decode(batch: int = 8, context_len: int = 32768, num_splits: int = 64,
 
 def mixed_int8(num_prefill: int = 4, chunk: int = 512, prefix: int = 1536, num_decode: int = 124,
                lo: int = 256, hi: int = 4096, max_tokens_per_split: int = 512,
-               seed: int = 1905, kv_dtype: str = I8) -> Step:
+               seed: int = 1905, kv_dtype: str = I8, values_seed: int | None = None) -> Step:
     """Mixed chunked-prefill + decode step over an int8 (or, with ``kv_dtype=
     "fp8"``, an fp8; with ``"bf16"``, a bf16 one of the same shape) KV cache: ``num_prefill``
     sequences with a ``chunk``-row causal chunk after a ``prefix``-token cached
     prefix, plus ``num_decode`` decode rows with n uniform in [256, 4096].
     16q/8kv/128, q and the new K/V rows bf16 (quantized by the cache write),
-    bs=16, pool = blocks needed, shuffled; decode splits ``ceil(n / 512)``."""
+    bs=16, pool = blocks needed, shuffled; decode splits ``ceil(n / 512)``.
+    ``values_seed`` draws other values over the same shapes and tables."""
     rng = np.random.default_rng(np.random.SeedSequence([seed, 7]))
     dec = rng.integers(lo, hi, size=num_decode, endpoint=True)
     ctx = np.concatenate([np.full(num_prefill, prefix + chunk), dec]).astype(np.int64)
@@ -282,4 +283,4 @@ def mixed_int8(num_prefill: int = 4, chunk: int = 512, prefix: int = 1536, num_d
     name = {I8: "mixed_int8", FP8: "mixed_fp8", BF16: "mixed_bf16"}[kv_dtype]
     return make_step(name, ctx, ql, num_q_heads=16, num_kv_heads=8,
                      head_dim=128, q_dtype=BF16, kv_dtype=kv_dtype, src_dtype=BF16,
-                     num_splits=splits_for(ctx, max_tokens_per_split), seed=seed)
+                     num_splits=splits_for(ctx, max_tokens_per_split), seed=seed, values_seed=values_seed)
